@@ -1,0 +1,350 @@
+"""Pins of the fp64 oracle against what the mathematics and the pages fix.
+
+Every test here runs on the CPU.  None compares the oracle with itself through
+a retyped formula: each checks a closed form, an invariant, a library route
+(torch / numpy in fp64) or a value printed on the pages.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, video_grid
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+# --------------------------------------------------------------------------------------
+# Workload geometry: the pages' worked example
+# --------------------------------------------------------------------------------------
+
+def test_geometry_worked_example():
+    with open(os.path.join(GOLDEN, "geometry.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        grid = video_grid(c["frames"], c["height"], c["width"])
+        assert list(grid) == c["grid"]
+        assert grid[0] * grid[1] * grid[2] == c["S"]
+        if "S_mod_8" in c:
+            assert c["S"] % 8 == c["S_mod_8"]
+
+
+def test_workload_table():
+    sizes = {w.name: (w.Nv, w.S, w.n_chunks) for w in WORKLOADS}
+    assert sizes["tiny"] == (240, 256, 4)
+    assert sizes["lite-clip"] == (3024, 3216, 7)
+    assert sizes["image-dit"] == (4096, 4352, 1)
+    assert sizes["pro-clip"] == (51840, 52608, 13)
+    assert sizes["long-video"] == (118800, 119056, 15)
+    for w in WORKLOADS:
+        assert sum(w.split) == w.D
+
+
+# --------------------------------------------------------------------------------------
+# Rounding to storage formats
+# --------------------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    # Values exactly representable in fp32: a single RNE step to bf16, which
+    # torch's fp32 -> bf16 conversion performs.
+    x32 = np.concatenate([
+        RNG.standard_normal(20000).astype(np.float32),
+        (RNG.standard_normal(2000) * 1e-38).astype(np.float32),   # subnormal range
+        (RNG.standard_normal(2000) * 1e38).astype(np.float32),
+        np.array([3.3895314e38, -3.3895314e38, 3.4e38], dtype=np.float32),
+    ])
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x32.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_round_bf16_ties_to_even():
+    one = 1.0
+    assert oracle.round_bf16(one + 2.0 ** -8)[()] == 1.0              # tie -> even (down)
+    assert oracle.round_bf16(one + 3 * 2.0 ** -8)[()] == 1.0 + 2.0 ** -6  # tie -> even (up)
+    assert oracle.round_bf16(one + 2.0 ** -8 + 2.0 ** -40)[()] == 1.0 + 2.0 ** -7
+    assert oracle.round_bf16(2.0 ** -134)[()] == 0.0                   # half the min subnormal
+    assert oracle.round_bf16(3 * 2.0 ** -134)[()] == 2.0 ** -132
+    assert np.isinf(oracle.round_bf16(3.5e38)[()])
+
+
+# --------------------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------------------
+
+SPLIT = (16, 24, 24)
+THETA = 10000.0
+
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def test_rope_identity_at_origin():
+    x = _rand(64)
+    assert np.array_equal(oracle.rope_vec(x, (0, 0, 0), SPLIT, THETA), x)
+
+
+def test_rope_preserves_pair_norms():
+    x = _rand(64)
+    y = oracle.rope_vec(x, (3, 7, 11), SPLIT, THETA)
+    nx = x.reshape(32, 2)
+    ny = y.reshape(32, 2)
+    np.testing.assert_allclose(np.hypot(ny[:, 0], ny[:, 1]), np.hypot(nx[:, 0], nx[:, 1]),
+                               rtol=1e-14)
+
+
+def test_rope_inverse():
+    x = _rand(128)
+    sp = (32, 48, 48)
+    y = oracle.rope_vec(oracle.rope_vec(x, (5, 9, 33), sp, THETA), (-5, -9, -33), sp, THETA)
+    np.testing.assert_allclose(y, x, atol=1e-13)
+
+
+def test_rope_relative_position():
+    q, k = _rand(64), _rand(64)
+    p, pp, delta = np.array([1, 4, 9]), np.array([0, 7, 2]), np.array([6, -3, 13])
+    a = oracle.rope_vec(q, p, SPLIT, THETA) @ oracle.rope_vec(k, pp, SPLIT, THETA)
+    b = oracle.rope_vec(q, p + delta, SPLIT, THETA) @ oracle.rope_vec(k, pp + delta, SPLIT, THETA)
+    assert abs(a - b) < 1e-12
+    # and it does depend on p - p'
+    c = oracle.rope_vec(q, p + np.array([1, 0, 0]), SPLIT, THETA) @ oracle.rope_vec(k, pp, SPLIT,
+                                                                                     THETA)
+    assert abs(a - c) > 1e-3
+
+
+def test_rope_first_pair_of_each_axis_rotates_by_position():
+    # The first pair of every axis segment has frequency theta^0 = 1, so a unit
+    # vector on it turns by exactly p_axis radians, counter-clockwise.
+    pos = (2, 5, 11)
+    for axis, off in enumerate((0, 16, 40)):
+        x = np.zeros(64)
+        x[off] = 1.0
+        y = oracle.rope_vec(x, pos, SPLIT, THETA)
+        want = np.zeros(64)
+        want[off], want[off + 1] = math.cos(pos[axis]), math.sin(pos[axis])
+        np.testing.assert_allclose(y, want, atol=1e-15)
+
+
+def test_rope_matches_complex_multiplication():
+    # Library route for the rotation itself: pairs as complex numbers times
+    # e^{i phi}, with phi from the per-axis frequency ladder.
+    sp = (32, 48, 48)
+    x = _rand(128)
+    pos = (7, 13, 40)
+    phis = []
+    for a, d in enumerate(sp):
+        j = torch.arange(d // 2, dtype=torch.float64)
+        phis.append(pos[a] * torch.pow(torch.tensor(THETA, dtype=torch.float64), -2 * j / d))
+    phi = torch.cat(phis)
+    z = torch.view_as_complex(torch.from_numpy(x).reshape(64, 2).contiguous())
+    want = torch.view_as_real(z * torch.polar(torch.ones_like(phi), phi)).reshape(128).numpy()
+    np.testing.assert_allclose(oracle.rope_vec(x, pos, sp, THETA), want, atol=1e-13)
+
+
+def test_rope3d_token_positions_row_major():
+    grid = (2, 3, 5)
+    x = _rand(1, 30, 2, 64)
+    y = oracle.rope3d(x, grid, SPLIT, THETA)
+    for n in (0, 1, 4, 5, 14, 15, 29):
+        t, h, w = np.unravel_index(n, grid)
+        for hd in range(2):
+            np.testing.assert_array_equal(y[0, n, hd],
+                                          oracle.rope_vec(x[0, n, hd], (t, h, w), SPLIT, THETA))
+
+
+def test_rope_2d_and_single_frame():
+    x = _rand(1, 16, 1, 128)
+    y2d = oracle.rope3d(x, (1, 4, 4), (0, 64, 64), THETA)
+    y3d = oracle.rope3d(x, (1, 4, 4), (32, 48, 48), THETA)
+    # t = 0 for every token: the t segment of the 3-D split is untouched
+    np.testing.assert_array_equal(y3d[..., :32], x[..., :32])
+    assert not np.allclose(y2d[..., 64:], x[..., 64:])
+    with pytest.raises(ValueError):
+        oracle.rope3d(x, (1, 4, 5), (32, 48, 48), THETA)
+
+
+# --------------------------------------------------------------------------------------
+# Joint concat + permute
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32, np.float64])
+def test_permute_matches_numpy(dtype):
+    segs = [(RNG.integers(0, 65535, size=(2, n, 3, 8))).astype(dtype) for n in (17, 5, 0, 9)]
+    out = oracle.joint_concat_permute(segs)
+    want = np.concatenate(segs, axis=1).transpose(0, 2, 1, 3)
+    assert out.dtype == want.dtype and np.array_equal(out, want)
+
+
+def test_permute_inverse():
+    segs = [RNG.standard_normal((1, n, 4, 16)) for n in (11, 3)]
+    out = oracle.joint_concat_permute(segs)
+    back = out.transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(back[:, :11], segs[0])
+    np.testing.assert_array_equal(back[:, 11:], segs[1])
+
+
+# --------------------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------------------
+
+def _qkv(B, H, Sq, Skv, D):
+    return _rand(B, H, Sq, D), _rand(B, H, Skv, D), _rand(B, H, Skv, D)
+
+
+def test_attention_single_key_returns_value():
+    q, k, v = _qkv(1, 2, 5, 1, 16)
+    out, lse = oracle.attention(q, k, v, 0.25)
+    np.testing.assert_array_equal(out, np.broadcast_to(v, out.shape))
+    np.testing.assert_allclose(lse, 0.25 * np.einsum("bhqd,bhkd->bhq", q, k), rtol=1e-15)
+
+
+def test_attention_identical_keys_give_mean_value():
+    q, k, v = _qkv(1, 2, 7, 13, 32)
+    k[:] = k[:, :, :1]
+    out, lse = oracle.attention(q, k, v, 0.3)
+    np.testing.assert_allclose(out, np.broadcast_to(v.mean(axis=2, keepdims=True), out.shape),
+                               atol=1e-14)
+    s = 0.3 * np.einsum("bhqd,bhd->bhq", q, k[:, :, 0])
+    np.testing.assert_allclose(lse, s + math.log(13), rtol=1e-14)
+
+
+def test_attention_zero_query_is_uniform():
+    q, k, v = _qkv(1, 1, 3, 40, 8)
+    q[:] = 0
+    out, lse = oracle.attention(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0, 0], np.broadcast_to(v[0, 0].mean(0), (3, 8)), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(40), rtol=1e-15)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 4), (1, 2, 9, 17, 8), (2, 3, 33, 64, 64),
+                                   (1, 1, 64, 48, 128)])
+def test_attention_matches_torch_softmax(shape):
+    B, H, Sq, Skv, D = shape
+    q, k, v = _qkv(B, H, Sq, Skv, D)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = oracle.attention(q, k, v, scale)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    logits = (tq @ tk.transpose(-1, -2)) * scale
+    want = torch.softmax(logits, dim=-1) @ tv
+    np.testing.assert_allclose(out, want.numpy(), atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), atol=1e-13)
+
+
+def test_attention_hard_max_limit():
+    q, k, v = _qkv(1, 1, 4, 30, 16)
+    out, _ = oracle.attention(q, k, v, 1e5)
+    amax = np.argmax(np.einsum("qd,kd->qk", q[0, 0], k[0, 0]), axis=1)
+    np.testing.assert_allclose(out[0, 0], v[0, 0][amax], atol=1e-12)
+
+
+def test_attention_kv_permutation_invariance():
+    q, k, v = _qkv(1, 2, 11, 37, 16)
+    perm = RNG.permutation(37)
+    a = oracle.attention(q, k, v, 0.25)
+    b = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.25)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13)
+
+
+def test_attention_query_rows_independent():
+    q, k, v = _qkv(2, 3, 19, 23, 16)
+    out, lse = oracle.attention(q, k, v, 0.25)
+    rows = np.array([0, 5, 18, 19, 40, 113, 2 * 3 * 19 - 1])
+    o_r, l_r = oracle.attention_rows(q, k, v, rows, 0.25)
+    np.testing.assert_array_equal(o_r, out.reshape(-1, 16)[rows])
+    np.testing.assert_array_equal(l_r, lse.reshape(-1)[rows])
+
+
+@pytest.mark.parametrize("kv_chunk", [1, 3, 7, 16, 50, 51, 0, 1000])
+def test_chunked_plus_merge_equals_unchunked(kv_chunk):
+    q, k, v = _qkv(1, 2, 9, 51, 16)
+    q *= 3.0  # sharper softmax: partial maxima differ between chunks
+    a_out, a_lse = oracle.attention(q, k, v, 0.25)
+    b_out, b_lse = oracle.attention_chunked(q, k, v, 0.25, kv_chunk)
+    np.testing.assert_allclose(b_out, a_out, atol=1e-12)
+    np.testing.assert_allclose(b_lse, a_lse, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# LSE merge
+# --------------------------------------------------------------------------------------
+
+def test_lse_merge_equal_weights():
+    parts = _rand(2, 5, 8)
+    lse = np.full((2, 5), 1.7)
+    out, L = oracle.lse_merge(parts, lse)
+    np.testing.assert_allclose(out, parts.mean(0), atol=1e-15)
+    np.testing.assert_allclose(L, 1.7 + math.log(2), atol=1e-15)
+
+
+def test_lse_merge_ignores_empty_parts():
+    parts = _rand(3, 4, 8)
+    lse = RNG.standard_normal((3, 4))
+    lse[1] = -np.inf
+    parts[1] = 1e300  # weight exactly zero
+    out, L = oracle.lse_merge(parts, lse)
+    o2, L2 = oracle.lse_merge(parts[[0, 2]], lse[[0, 2]])
+    np.testing.assert_allclose(out, o2, atol=1e-14)
+    np.testing.assert_allclose(L, L2, atol=1e-14)
+    out3, L3 = oracle.lse_merge(parts[:1] * 0 + 5, np.full((1, 4), -np.inf))
+    assert np.all(out3 == 0) and np.all(np.isneginf(L3))
+
+
+@pytest.mark.parametrize("cuts", [(0, 20, 51), (0, 1, 2, 30, 51), (0, 51)])
+def test_lse_merge_of_kv_slices_equals_full_attention(cuts):
+    q, k, v = _qkv(1, 2, 6, 51, 16)
+    q *= 2.0
+    full_out, full_lse = oracle.attention(q, k, v, 0.25)
+    outs, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l_ = oracle.attention(q, k[:, :, a:b], v[:, :, a:b], 0.25)
+        outs.append(o)
+        lses.append(l_)
+    out, L = oracle.lse_merge(np.stack(outs), np.stack(lses))
+    np.testing.assert_allclose(out, full_out, atol=1e-12)
+    np.testing.assert_allclose(L, full_lse, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# Whole pipeline on a tiny joint sequence
+# --------------------------------------------------------------------------------------
+
+def test_pipeline_against_torch_route():
+    """prepare_qkv + attention against a torch fp64 route built from library
+    pieces (complex rotation, cat, permute, softmax) on a tiny joint sequence."""
+    grid, sp = (2, 2, 3), (16, 24, 24)
+    B, H, D = 1, 2, 64
+    segs = {n: [RNG.standard_normal((B, 12, H, D)), RNG.standard_normal((B, 5, H, D))]
+            for n in "qkv"}
+    q, k, v = oracle.prepare_qkv(segs["q"], segs["k"], segs["v"], grid, sp, THETA, "f32")
+    out, lse = oracle.attention(q, k, v, 0.125)
+
+    def rot(x):
+        t = torch.from_numpy(x)
+        pos = torch.stack(torch.meshgrid(*[torch.arange(g) for g in grid], indexing="ij"),
+                          -1).reshape(-1, 3).to(torch.float64)
+        phis = []
+        for a, d in enumerate(sp):
+            j = torch.arange(d // 2, dtype=torch.float64)
+            phis.append(pos[:, a:a + 1] * torch.pow(torch.tensor(THETA, dtype=torch.float64),
+                                                     -2 * j / d))
+        phi = torch.cat(phis, dim=1)[None, :, None, :]
+        z = torch.view_as_complex(t.reshape(B, 12, H, D // 2, 2).contiguous())
+        r = torch.view_as_real(z * torch.polar(torch.ones_like(phi), phi)).reshape(B, 12, H, D)
+        return r.to(torch.float32).to(torch.float64)
+
+    def joint(segs_, rope):
+        first = rot(segs_[0]) if rope else torch.from_numpy(segs_[0])
+        return torch.cat([first, torch.from_numpy(segs_[1])], dim=1).transpose(1, 2)
+
+    tq, tk, tv = joint(segs["q"], True), joint(segs["k"], True), joint(segs["v"], False)
+    logits = (tq @ tk.transpose(-1, -2)) * 0.125
+    want = torch.softmax(logits, -1) @ tv
+    np.testing.assert_allclose(out, want.numpy(), atol=1e-6)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).numpy(), atol=1e-6)
