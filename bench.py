@@ -1,0 +1,238 @@
+"""Throughput of the joint-sequence attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pro-clip]
+                    [--no-cpu-baseline] [--no-kernels]
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+  joint_concat_permute(Q segments, RoPE on video)  -> q [B,H,S,D]
+  joint_concat_permute(K segments, RoPE on video)  -> k
+  joint_concat_permute(V segments)                 -> v
+  attn_fwd(q, k, v, scale, kv_chunk)               -> out, lse
+(the chunked online softmax and the explicit log-sum-exp merge run inside
+attn_fwd).  `value` is attention TFLOP/s over the whole step, counting
+4*B*H*Sq*Skv*D flops per step.  The standalone rope3d_apply and lse_merge
+entry points are timed after the step loop on the same workload shapes and
+reported under "kernels".
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+MI355X_HBM_GBPS = 8000.0
+METRIC = "attention TFLOP/s (4·B·H·Sq·Skv·D) + % bf16 MFMA peak; ms/call at 52k tokens"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_traffic.md")
+ATTN_SRC = os.path.join(ROOT, "long_sequence_attention_rope3d_amd", "csrc", "attn_fwd_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _traffic_for_current_kernel():
+    """HBM bytes per attn_fwd launch from the committed rocprofv3 --pmc summary,
+    or None if there is none or the kernel source changed since it was taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, inp, n_rows: int):
+    """The fp64 oracle, as it is, on a bounded sample: RoPE of all of Q and K,
+    the re-layout, then attention for n_rows query rows spread over every
+    head.  Reported in the metric's unit (attention TFLOP/s of the sampled
+    rows over the whole oracle time)."""
+    import numpy as np
+    import oracle
+    from workloads.inputs import to_f64
+    rng = np.random.default_rng(w.seed + 7)
+    rows = np.sort(rng.choice(w.B * w.H * w.S, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    q, k, v = oracle.prepare_qkv([to_f64(s) for s in inp["q"]], [to_f64(s) for s in inp["k"]],
+                                 [to_f64(s) for s in inp["v"]], w.grid, w.split, w.theta,
+                                 "bf16" if w.dtype == "bf16" else "f32")
+    oracle.attention_rows(q, k, v, rows, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * n_rows * w.S * w.D
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_rows} query rows of {w.B * w.H * w.S} ({w.name}), with the fp64 RoPE "
+                      f"and re-layout of the full Q/K/V; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="pro-clip")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=3072)
+    ap.add_argument("--no-kernels", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note, not part of this library).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_sequence_attention_rope3d_amd as r3d
+    from workloads import by_name, make_inputs
+
+    w = by_name(args.workload)
+    dev = torch.device("cuda", 0)
+    log(f"workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} kv_chunk={w.kv_chunk} {w.dtype}")
+    t0 = time.perf_counter()
+    inp = make_inputs(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    segs = {n: [s.to(dev) for s in inp[n]] for n in "qkv"}
+    rope = r3d.Rope3D(w.grid, w.split, w.theta)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = torch.empty((w.B, w.H, w.S, w.D), dtype=tdt, device=dev)
+    k, v, out = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        r3d.joint_concat_permute(segs["q"], rope, out=q)
+        r3d.joint_concat_permute(segs["k"], rope, out=k)
+        r3d.joint_concat_permute(segs["v"], None, out=v)
+        if ev is not None:
+            ev[0].record(stream)
+        r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk, out=out, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in events]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.attn_flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (attn_avg_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms, attn_fwd {attn_avg_ms:.3f} ms (min {min(attn_ms):.3f}) "
+        f"= {achieved:.1f} TFLOP/s ({100 * achieved / MI355X_BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
+    assert torch.isfinite(out.float()).all().item()
+
+    kernels = {}
+    if not args.no_kernels:
+        kernels = time_side_kernels(torch, r3d, w, segs, q, lse, rope, dev, stream)
+
+    traffic_bytes = _traffic_for_current_kernel()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_bytes, "kernel": "attn_fwd (attn_bf16_kernel<128>)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del segs
+        torch.cuda.synchronize()
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows ...")
+        cpu = cpu_baseline(w, inp, args.cpu_rows)
+        log(f"cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V shaped like the workload; no datasets)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.S, "Skv": w.S, "D": w.D,
+                   "video_grid": list(w.grid), "joint": dict(w.joint), "kv_chunk": w.kv_chunk,
+                   "n_chunks": w.n_chunks, "parallelism": "single-gpu"},
+        "attn_ms_per_call": round(attn_avg_ms, 4),
+        "attn_tflops": round(achieved, 2),
+        "pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def time_side_kernels(torch, r3d, w, segs, q, lse, rope, dev, stream, reps: int = 5):
+    """HBM-bound entry points on this workload's shapes, as GB/s of
+    algorithmic bytes (each input read once, each output written once)."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    es = 2 if w.dtype == "bf16" else 4
+    n_all = w.B * w.H * w.S * w.D
+    n_vid = w.B * w.H * w.Nv * w.D
+    # fused RoPE + joint concat + re-layout of one tensor (Q)
+    ms = timed(lambda: r3d.joint_concat_permute(segs["q"], rope, out=q))
+    res["joint_concat_permute_rope"] = {"ms": round(ms, 4), "bytes": 2 * n_all * es,
+                                        "GBps": round(2 * n_all * es / ms / 1e6, 1)}
+    ms = timed(lambda: r3d.joint_concat_permute(segs["v"], None, out=q))
+    res["joint_concat_permute"] = {"ms": round(ms, 4), "bytes": 2 * n_all * es,
+                                   "GBps": round(2 * n_all * es / ms / 1e6, 1)}
+    x = segs["q"][0]
+    y = torch.empty_like(x)
+    ms = timed(lambda: r3d.rope3d_apply(x, w.grid, w.split, w.theta, out=y))
+    res["rope3d_apply"] = {"ms": round(ms, 4), "bytes": 2 * n_vid * es,
+                           "GBps": round(2 * n_vid * es / ms / 1e6, 1)}
+    del y
+    # ring-form combine: one fp32 partial per kv_chunk
+    n = w.n_chunks
+    parts = torch.empty((n, w.B, w.H, w.S, w.D), dtype=torch.float32, device=dev).normal_()
+    lparts = torch.empty((n, w.B, w.H, w.S), dtype=torch.float32, device=dev).normal_()
+    mout = torch.empty((w.B, w.H, w.S, w.D), dtype=q.dtype, device=dev)
+    nbytes = n * w.B * w.H * w.S * (w.D * 4 + 4) + w.B * w.H * w.S * (w.D * es + 4)
+    ms = timed(lambda: r3d.lse_merge(parts, lparts, out=mout, lse_out=lse))
+    res["lse_merge"] = {"ms": round(ms, 4), "n_parts": n, "bytes": nbytes,
+                        "GBps": round(nbytes / ms / 1e6, 1)}
+    del parts, lparts, mout
+    for kname, r in res.items():
+        r["frac_hbm_peak"] = round(r["GBps"] / MI355X_HBM_GBPS, 4)
+        log(f"{kname}: {r['ms']:.3f} ms, {r['GBps']:.0f} GB/s")
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * r3d_attn.h — C ABI of librope3d_attn.so: joint-sequence attention with 3-D
+ * rotary embeddings for video(+audio) diffusion transformers, on one AMD
+ * MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Buffers are DEVICE pointers owned by the caller, contiguous (row-major)
+ *    in the layout stated per call, 16-byte aligned.  The library allocates
+ *    nothing, keeps no pointer after it returns, and creates no stream.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    null stream).  A return of R3D_OK means the work was enqueued; errors of
+ *    the kernels themselves surface on the stream like any HIP error.
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    failure nothing is launched, the return is a negative r3d_status, and
+ *    r3d_last_error() describes it.  No C++ exception crosses the ABI.
+ *  - Outputs must not alias inputs unless a call says otherwise.
+ *  - Thread safety: calls may be made from several host threads; the error
+ *    message is per thread.
+ */
+#ifndef R3D_ATTN_H
+#define R3D_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define R3D_API __attribute__((visibility("default")))
+#else
+#define R3D_API
+#endif
+
+typedef enum {
+  R3D_OK = 0,
+  R3D_EINVAL = -1,        /* bad argument: NULL/misaligned pointer, size, split, aliasing */
+  R3D_EUNSUPPORTED = -2,  /* valid request that this build has no kernel for (D, dtype) */
+  R3D_EHIP = -3           /* the HIP runtime reported an error at launch */
+} r3d_status;
+
+typedef enum {
+  R3D_F32 = 0,   /* IEEE binary32 */
+  R3D_BF16 = 1   /* bfloat16, stored as the upper 16 bits of binary32 */
+} r3d_dtype;
+
+/*
+ * 3-D rotary embedding of the video tokens.  The pages apply
+ * apply_rotary_emb_wan(query/key, freqs_cos, freqs_sin) to Q and K (never V)
+ * before the transpose to [B, N, S, D], with rotary tables indexed by
+ * sequence position ("Context Parallelism in vLLM Omni Neuron",
+ * §Self-Attention with Context Parallelism, §Positional Embedding Handling).
+ * The formula itself is not printed there; this library's definition:
+ *  - video token n of a segment sits at grid position (t, h, w) with
+ *    n = (t*grid_h + h)*grid_w + w (row-major latent grid, §Problem);
+ *  - the head dimension is split into contiguous [d_t | d_h | d_w];
+ *  - in the segment of axis a, pair (off_a + 2j, off_a + 2j + 1) turns by
+ *    angle p_a * theta^(-2j/d_a), i.e. (x0, x1) -> (x0 c - x1 s, x0 s + x1 c);
+ *  - d_a may be 0 (2-D RoPE on an image uses d_t = 0).
+ * Angles, sin/cos and the rotation are computed in fp64 and the result is
+ * rounded once to the storage dtype (round-to-nearest-even).
+ */
+typedef struct {
+  int64_t grid_t, grid_h, grid_w;  /* video tokens = grid_t*grid_h*grid_w       */
+  int32_t d_t, d_h, d_w;           /* even, >= 0, d_t + d_h + d_w == D          */
+  double theta;                    /* base, finite and > 0 (10000 here)         */
+} r3d_rope_desc;
+
+/*
+ * r3d_rope3d_apply — rotate the video tokens of Q or K.
+ *   x, y : [B, Nv, H, D] in `dtype`; y == x (in place) is allowed, any other
+ *          overlap is rejected.  Nv must equal the grid product of `rope`.
+ *   D    : 64 or 128.
+ * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, split/grid mismatch,
+ * partial overlap), R3D_EUNSUPPORTED (D or dtype), R3D_EHIP.
+ */
+R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t Nv,
+                             int64_t H, int64_t D, const r3d_rope_desc* rope, void* stream);
+
+/*
+ * r3d_joint_concat_permute — joint concat + sequence->head re-layout.
+ * The single-device form of the Ulysses input all-to-all followed by
+ * .transpose(1, 2) ("Context Parallelism in vLLM Omni Neuron",
+ * §Self-Attention with Context Parallelism; xDiT PR "Adds support for
+ * KV-cache and joint tensors to USP method": joint tensors are concatenated
+ * to the visual sequence inside attention):
+ *     out[b, h, off_i + s, :] = segs[i][b, s, h, :],  off_i = sum_{j<i} seg_len[j]
+ *   segs    : HOST array of n_segs DEVICE pointers, segment i is [B, seg_len[i], H, D]
+ *             (video first, then audio, then text); a segment of length 0 may be NULL.
+ *   seg_len : HOST array of n_segs lengths >= 0, sum S > 0.  1 <= n_segs <= 8.
+ *   out     : [B, H, S, D] in `dtype`; must not overlap any segment.
+ *   rope_seg0 : NULL -> a pure copy, bit-exact.  Otherwise segment 0 (the video
+ *             tokens, seg_len[0] == grid product) is rotated as r3d_rope3d_apply
+ *             would while it is copied (one HBM round trip instead of two);
+ *             the other segments are copied bit-exactly (joint tokens carry no
+ *             position).
+ * Errors: R3D_EINVAL, R3D_EUNSUPPORTED (D not 64/128 with RoPE, dtype), R3D_EHIP.
+ * Without RoPE any D >= 1 whose row is a multiple of 16 bytes is accepted.
+ */
+R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg_len,
+                                     int32_t n_segs, void* out, int32_t dtype, int64_t B,
+                                     int64_t H, int64_t D, const r3d_rope_desc* rope_seg0,
+                                     void* stream);
+
+/*
+ * r3d_attn_fwd — full non-causal multi-head attention, blockwise.
+ * ("Context Parallelism in vLLM Omni Neuron", §Self-Attention:
+ * _nf_attend(query, key, value, scale) on [B, N, S, D]; §Ring attention and
+ * §Full K/V AllGather: local Q attends the full K/V, one K/V chunk at a time;
+ * xDiT PR #586: _attention(query, key, value, dropout_p, is_causal) with no
+ * dropout and is_causal false for DiT self-attention.)
+ *   q   : [B, H, Sq, D];  k, v : [B, H, Skv, D];  all in `dtype`.
+ *   out : [B, H, Sq, D] in `dtype` (bf16 rounded to nearest-even from fp32).
+ *   lse : [B, H, Sq] fp32 natural-log log-sum-exp of the scaled logits, or NULL.
+ *   scale : logit multiplier (finite; 1/sqrt(D) in every workload here).
+ *   kv_chunk : keys are processed in chunks [c*kv_chunk, (c+1)*kv_chunk); inside a
+ *           chunk the softmax is online (running max / sum, rescaled per key tile);
+ *           each finished chunk (O_c = acc/l, lse_c = m + ln l) is combined into the
+ *           running result by an explicit log-sum-exp merge
+ *             L' = ln(e^L + e^lse_c), O = O e^(L-L') + O_c e^(lse_c-L'),
+ *           in registers, with no partials written to memory.  0 or >= Skv means one
+ *           chunk.  The result equals softmax(q k^T scale) v for every kv_chunk (up to
+ *           rounding).
+ *   D   : 64 or 128.  dtype R3D_BF16 runs on bf16 MFMA with fp32 accumulation and an
+ *         fp32 softmax (P rounded to bf16 for the PV product); R3D_F32 is an all-fp32
+ *         path.
+ * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
+ * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype), R3D_EHIP.
+ */
+R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                         int64_t kv_chunk, int32_t dtype, void* stream);
+
+/*
+ * r3d_lse_merge — combine n partial attention results of the same queries
+ * against disjoint key sets (the ring-attention combine: each ring step
+ * attends one K/V shard, "Context Parallelism in vLLM Omni Neuron",
+ * §Ring attention; xDiT PR #586, ring_attn):
+ *     L = ln sum_i e^(lse_i),   out = sum_i e^(lse_i - L) o_i
+ *   o_parts   : [n_parts, B, H, S, D] in parts_dtype (F32 or BF16).
+ *   lse_parts : [n_parts, B, H, S] fp32, natural log; -inf marks an empty part
+ *               (weight 0).  A row whose parts are all -inf gets out = 0, L = -inf.
+ *   out       : [B, H, S, D] in out_dtype;  lse_out : [B, H, S] fp32 or NULL.
+ *   1 <= n_parts <= 64; D a multiple of 8, <= 256.
+ * Errors: R3D_EINVAL, R3D_EUNSUPPORTED, R3D_EHIP.
+ */
+R3D_API int r3d_lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,
+                          int32_t parts_dtype, void* out, float* lse_out, int32_t out_dtype,
+                          int64_t B, int64_t H, int64_t S, int64_t D, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+R3D_API const char* r3d_last_error(void);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+R3D_API const char* r3d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* R3D_ATTN_H */

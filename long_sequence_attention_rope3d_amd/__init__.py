@@ -1,0 +1,226 @@
+"""Joint-sequence attention with 3-D RoPE on one AMD MI355X (gfx950).
+
+Thin ctypes binding over ``lib/librope3d_attn.so`` (C ABI in
+``include/r3d_attn.h``).  This module only marshals arguments: it takes
+torch tensors that already live on the GPU, passes their device pointers,
+sizes and torch's current HIP stream to the library, and maps error codes to
+exceptions.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  If the library is missing, importing this
+package raises ImportError (build it with ``python -m
+long_sequence_attention_rope3d_amd.build``).
+
+Calls (same names as the C entry points without the ``r3d_`` prefix):
+  rope3d_apply(x, grid, split, theta=10000.0, out=None)
+  joint_concat_permute(segs, rope=None, out=None)
+  attn_fwd(q, k, v, scale=None, kv_chunk=0, out=None, lse=None, return_lse=True)
+  lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "lse_merge", "joint_attention", "Rope3D",
+           "library_path", "R3D_OK", "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "librope3d_attn.so")
+
+R3D_OK, R3D_EINVAL, R3D_EUNSUPPORTED, R3D_EHIP = 0, -1, -2, -3
+_F32, _BF16 = 0, 1
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class _RopeDesc(ctypes.Structure):
+    _fields_ = [("grid_t", ctypes.c_int64), ("grid_h", ctypes.c_int64), ("grid_w", ctypes.c_int64),
+                ("d_t", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32),
+                ("theta", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m long_sequence_attention_rope3d_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, ctypes.POINTER(_RopeDesc), P]
+    lib.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64,
+                                             ctypes.POINTER(_RopeDesc), P]
+    lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P]
+    lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
+    for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd", "r3d_lse_merge"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.r3d_last_error.restype = ctypes.c_char_p
+    lib.r3d_last_error.argtypes = []
+    lib.r3d_version.restype = ctypes.c_char_p
+    lib.r3d_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+@dataclass(frozen=True)
+class Rope3D:
+    """Video token grid (t, h, w) and the split of D over the three axes."""
+    grid: Tuple[int, int, int]
+    split: Tuple[int, int, int]
+    theta: float = 10000.0
+
+    def desc(self) -> _RopeDesc:
+        return _RopeDesc(int(self.grid[0]), int(self.grid[1]), int(self.grid[2]), int(self.split[0]),
+                         int(self.split[1]), int(self.split[2]), float(self.theta))
+
+
+def _check(status: int, what: str) -> None:
+    if status == R3D_OK:
+        return
+    msg = (_lib.r3d_last_error() or b"").decode(errors="replace")
+    if status in (R3D_EINVAL, R3D_EUNSUPPORTED):
+        raise ValueError(f"{what}: {msg}")
+    raise RuntimeError(f"{what}: {msg} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def rope3d_apply(x: torch.Tensor, grid, split, theta: float = 10000.0,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rotate video tokens x [B, Nv, H, D] by their (t, h, w) grid position.
+    ``out`` may be ``x`` itself (in place)."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B, Nv, H, D]")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    B, Nv, H, D = x.shape
+    desc = Rope3D(tuple(grid), tuple(split), theta).desc()
+    _check(_lib.r3d_rope3d_apply(_dev(x, "x"), _dev(out, "out"), _dtype_code(x), B, Nv, H, D,
+                                 ctypes.byref(desc), _stream(x)), "rope3d_apply")
+    return out
+
+
+def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """segs: [B, S_i, H, D] tensors (video first) -> [B, H, sum S_i, D].
+    With ``rope``, segment 0 is rotated while it is copied."""
+    segs = list(segs)
+    if not segs:
+        raise ValueError("need at least one segment")
+    B, _, H, D = segs[0].shape
+    dt = segs[0].dtype
+    for s in segs:
+        if s.dim() != 4 or s.shape[0] != B or s.shape[2] != H or s.shape[3] != D or s.dtype != dt:
+            raise ValueError("segments must be [B, S_i, H, D] with equal B, H, D and dtype")
+        if s.device != segs[0].device:
+            raise ValueError("segments must be on one device")
+    S = sum(int(s.shape[1]) for s in segs)
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=dt, device=segs[0].device)
+    if tuple(out.shape) != (B, H, S, D) or out.dtype != dt:
+        raise ValueError("out must be [B, H, S, D] of the segments' dtype")
+    ptrs = (ctypes.c_void_p * len(segs))(
+        *[(_dev(s, "segment") if s.shape[1] > 0 else None) for s in segs])
+    lens = (ctypes.c_int64 * len(segs))(*[int(s.shape[1]) for s in segs])
+    desc = rope.desc() if rope is not None else None
+    _check(_lib.r3d_joint_concat_permute(ctypes.cast(ptrs, ctypes.c_void_p),
+                                         ctypes.cast(lens, ctypes.c_void_p), len(segs),
+                                         _dev(out, "out"), _dtype_code(out), B, H, D,
+                                         ctypes.byref(desc) if desc is not None else None,
+                                         _stream(out)), "joint_concat_permute")
+    return out
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+             kv_chunk: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             return_lse: bool = True):
+    """Blockwise non-causal attention. q [B,H,Sq,D], k/v [B,H,Skv,D] ->
+    (out [B,H,Sq,D], lse [B,H,Sq] fp32 natural log) — or out alone if
+    return_lse is False and no lse buffer is given."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError("k and v must be [B, H, Skv, D] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be [B, H, Sq] float32")
+    _check(_lib.r3d_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                             _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                             float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+              out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+              return_lse: bool = True):
+    """o_parts [n,B,H,S,D], lse_parts [n,B,H,S] fp32 -> (out [B,H,S,D], lse [B,H,S])."""
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("o_parts must be [n,B,H,S,D] and lse_parts [n,B,H,S]")
+    n, B, H, S, D = o_parts.shape
+    if tuple(lse_parts.shape) != (n, B, H, S) or lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32 [n, B, H, S]")
+    out_dtype = out_dtype or o_parts.dtype
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=out_dtype, device=o_parts.device)
+    if tuple(out.shape) != (B, H, S, D):
+        raise ValueError("out must be [B, H, S, D]")
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
+    _check(_lib.r3d_lse_merge(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n,
+                              _dtype_code(o_parts), _dev(out, "out"),
+                              _dev(lse_out, "lse_out") if lse_out is not None else None,
+                              _dtype_code(out), B, H, S, D, _stream(out)), "lse_merge")
+    return (out, lse_out) if lse_out is not None else out
+
+
+def joint_attention(q_segs: Sequence[torch.Tensor], k_segs: Sequence[torch.Tensor],
+                    v_segs: Sequence[torch.Tensor], rope: Optional[Rope3D], scale: Optional[float] = None,
+                    kv_chunk: int = 0, return_lse: bool = True):
+    """The whole path for one attention call: per-segment [B, S_i, H, D] Q/K/V
+    (video first) -> RoPE on the video part of Q and K fused into the joint
+    concat + [B, H, S, D] re-layout -> blockwise attention.  Returns
+    attn_fwd's result in [B, H, S, D]."""
+    q = joint_concat_permute(q_segs, rope)
+    k = joint_concat_permute(k_segs, rope)
+    v = joint_concat_permute(v_segs, None)
+    return attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, return_lse=return_lse)

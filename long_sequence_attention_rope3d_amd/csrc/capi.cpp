@@ -1,0 +1,251 @@
+// capi.cpp — the C ABI of librope3d_attn.so (declared in include/r3d_attn.h).
+//
+// Every argument is validated here, on the host, before anything is
+// enqueued; the kernels assume what is checked here (sizes, alignment,
+// supported head dims, non-overlap).  No exception crosses the ABI.
+#include "r3d_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return R3D_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(R3D_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a*b*... with overflow detection; sizes must be positive.
+bool mul_ok(int64_t& acc, int64_t x) {
+  int64_t r;
+  if (x < 0 || __builtin_mul_overflow(acc, x, &r)) return false;
+  acc = r;
+  return true;
+}
+
+bool product(int64_t& out, std::initializer_list<int64_t> xs) {
+  int64_t acc = 1;
+  for (int64_t x : xs)
+    if (!mul_ok(acc, x)) return false;
+  out = acc;
+  return true;
+}
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int elt_size(int32_t dt) { return dt == R3D_F32 ? 4 : dt == R3D_BF16 ? 2 : 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // 1 Ti elements per tensor
+
+// A 1-D launch of `blocks` blocks of `threads` work-items must stay below
+// 2^32 work-items in total.
+bool launch_fits(int64_t blocks, int64_t threads) {
+  return blocks > 0 && blocks <= (int64_t(1) << 31) - 1 && blocks * threads < (int64_t(1) << 32);
+}
+
+// Builds the per-pair frequency/axis table of a rotary descriptor for head
+// dim D and checks it against the video token count Nv.
+int build_rope(const r3d_rope_desc* rope, int64_t D, int64_t Nv, r3d::RopeArgs& out) {
+  if (!rope) return fail(R3D_EINVAL, "rope descriptor is NULL");
+  if (rope->grid_t < 1 || rope->grid_h < 1 || rope->grid_w < 1)
+    return fail(R3D_EINVAL, "rope grid (%lld,%lld,%lld) must be >= 1 on every axis",
+                (long long)rope->grid_t, (long long)rope->grid_h, (long long)rope->grid_w);
+  int64_t n;
+  if (!product(n, {rope->grid_t, rope->grid_h, rope->grid_w}) || n != Nv)
+    return fail(R3D_EINVAL, "video token count %lld != grid product %lld*%lld*%lld", (long long)Nv,
+                (long long)rope->grid_t, (long long)rope->grid_h, (long long)rope->grid_w);
+  const int32_t d[3] = {rope->d_t, rope->d_h, rope->d_w};
+  for (int a = 0; a < 3; ++a)
+    if (d[a] < 0 || (d[a] & 1))
+      return fail(R3D_EINVAL, "rope split (%d,%d,%d): every part must be even and >= 0", d[0], d[1], d[2]);
+  if ((int64_t)d[0] + d[1] + d[2] != D)
+    return fail(R3D_EINVAL, "rope split (%d,%d,%d) does not sum to D=%lld", d[0], d[1], d[2], (long long)D);
+  if (!(std::isfinite(rope->theta) && rope->theta > 0.0))
+    return fail(R3D_EINVAL, "rope theta must be finite and > 0");
+  if (D / 2 > r3d::kMaxPairs) return fail(R3D_EUNSUPPORTED, "RoPE supports D <= %d", 2 * r3d::kMaxPairs);
+  int p = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < d[a] / 2; ++j, ++p) {
+      out.omega[p] = std::pow(rope->theta, -2.0 * (double)j / (double)d[a]);
+      out.axis[p] = (int8_t)a;
+    }
+  for (; p < r3d::kMaxPairs; ++p) {
+    out.omega[p] = 0.0;
+    out.axis[p] = 0;
+  }
+  out.grid_h = rope->grid_h;
+  out.grid_w = rope->grid_w;
+  out.enabled = 1;
+  return R3D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+R3D_API const char* r3d_last_error(void) { return g_last_error.c_str(); }
+
+R3D_API const char* r3d_version(void) { return "0.1.0 gfx950"; }
+
+R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, int64_t Nv,
+                             int64_t H, int64_t D, const r3d_rope_desc* rope, void* stream) {
+  const int es = elt_size(dtype);
+  if (!es) return fail(R3D_EUNSUPPORTED, "rope3d_apply: unknown dtype %d", dtype);
+  if (!x || !y) return fail(R3D_EINVAL, "rope3d_apply: NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return fail(R3D_EINVAL, "rope3d_apply: pointers must be 16-byte aligned");
+  if (B <= 0 || Nv <= 0 || H <= 0 || D <= 0)
+    return fail(R3D_EINVAL, "rope3d_apply: B, Nv, H, D must be > 0");
+  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "rope3d_apply: D=%lld (supported: 64, 128)", (long long)D);
+  int64_t n;
+  if (!product(n, {B, Nv, H, D}) || n > kMaxElems) return fail(R3D_EINVAL, "rope3d_apply: tensor too large");
+  if (x != y && overlap(x, n * es, y, n * es))
+    return fail(R3D_EINVAL, "rope3d_apply: x and y overlap without being identical");
+  if (!launch_fits(((Nv + 7) / 8) * B, 256)) return fail(R3D_EINVAL, "rope3d_apply: B*Nv too large for one launch");
+  r3d::RopeArgs ra{};
+  int st = build_rope(rope, D, Nv, ra);
+  if (st != R3D_OK) return st;
+  return hip_status(r3d::launch_rope3d(x, y, dtype == R3D_BF16, B, Nv, H, D, ra, (hipStream_t)stream),
+                    "rope3d_apply");
+}
+
+R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg_len,
+                                     int32_t n_segs, void* out, int32_t dtype, int64_t B,
+                                     int64_t H, int64_t D, const r3d_rope_desc* rope_seg0,
+                                     void* stream) {
+  const int es = elt_size(dtype);
+  if (!es) return fail(R3D_EUNSUPPORTED, "joint_concat_permute: unknown dtype %d", dtype);
+  if (!segs || !seg_len) return fail(R3D_EINVAL, "joint_concat_permute: NULL segment arrays");
+  if (n_segs < 1 || n_segs > r3d::kMaxSegs)
+    return fail(R3D_EINVAL, "joint_concat_permute: n_segs=%d (1..%d)", n_segs, r3d::kMaxSegs);
+  if (!out || !aligned16(out)) return fail(R3D_EINVAL, "joint_concat_permute: out NULL or not 16-byte aligned");
+  if (B <= 0 || H <= 0 || D <= 0) return fail(R3D_EINVAL, "joint_concat_permute: B, H, D must be > 0");
+  if ((D * es) % 16 != 0)
+    return fail(R3D_EUNSUPPORTED, "joint_concat_permute: a row of D=%lld elements must be a multiple of 16 bytes",
+                (long long)D);
+  r3d::SegArgs sa{};
+  int64_t S = 0;
+  for (int i = 0; i < n_segs; ++i) {
+    if (seg_len[i] < 0) return fail(R3D_EINVAL, "joint_concat_permute: seg_len[%d] < 0", i);
+    if (seg_len[i] > 0 && (!segs[i] || !aligned16(segs[i])))
+      return fail(R3D_EINVAL, "joint_concat_permute: segment %d NULL or not 16-byte aligned", i);
+    sa.src[i] = segs[i];
+    sa.len[i] = seg_len[i];
+    sa.off[i] = S;
+    if (__builtin_add_overflow(S, seg_len[i], &S)) return fail(R3D_EINVAL, "joint_concat_permute: S overflows");
+  }
+  sa.n = n_segs;
+  sa.S = S;
+  if (S <= 0) return fail(R3D_EINVAL, "joint_concat_permute: total sequence length is 0");
+  int64_t n_out;
+  if (!product(n_out, {B, H, S, D}) || n_out > kMaxElems)
+    return fail(R3D_EINVAL, "joint_concat_permute: output too large");
+  if (!launch_fits(((S + 7) / 8) * B, 256))
+    return fail(R3D_EINVAL, "joint_concat_permute: B*S too large for one launch");
+  for (int i = 0; i < n_segs; ++i) {
+    int64_t ni;
+    product(ni, {B, seg_len[i], H, D});
+    if (overlap(segs[i], ni * es, out, n_out * es))
+      return fail(R3D_EINVAL, "joint_concat_permute: out overlaps segment %d", i);
+  }
+  r3d::RopeArgs ra{};
+  if (rope_seg0) {
+    if (D != 64 && D != 128)
+      return fail(R3D_EUNSUPPORTED, "joint_concat_permute: RoPE needs D in {64, 128}, got %lld", (long long)D);
+    int st = build_rope(rope_seg0, D, seg_len[0], ra);
+    if (st != R3D_OK) return st;
+  }
+  return hip_status(r3d::launch_permute(sa, out, dtype == R3D_BF16, B, H, D, ra, (hipStream_t)stream),
+                    "joint_concat_permute");
+}
+
+R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                         int64_t kv_chunk, int32_t dtype, void* stream) {
+  const int es = elt_size(dtype);
+  if (!es) return fail(R3D_EUNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
+  if (!q || !k || !v || !out) return fail(R3D_EINVAL, "attn_fwd: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(R3D_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
+    return fail(R3D_EINVAL, "attn_fwd: B, H, Sq, Skv, D must be > 0");
+  if (kv_chunk < 0) return fail(R3D_EINVAL, "attn_fwd: kv_chunk=%lld < 0", (long long)kv_chunk);
+  if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
+  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
+  int64_t nq, nk, bhq;
+  if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
+    return fail(R3D_EINVAL, "attn_fwd: tensor too large");
+  product(bhq, {B, H, Sq});
+  if (dtype == R3D_BF16 ? !launch_fits(B * H * ((Sq + 127) / 128), 256) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
+    return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
+  const void* ins[3] = {q, k, v};
+  const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(out, nq * es, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: out overlaps an input");
+    if (lse && overlap(lse, bhq * 4, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: lse overlaps an input");
+  }
+  if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "attn_fwd: lse overlaps out");
+  const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
+  hipError_t e;
+  if (dtype == R3D_BF16)
+    e = r3d::launch_attn_bf16(q, k, v, out, lse, B, H, Sq, Skv, D, scale, chunk, (hipStream_t)stream);
+  else
+    e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
+                             D, scale, chunk, (hipStream_t)stream);
+  return hip_status(e, "attn_fwd");
+}
+
+R3D_API int r3d_lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,
+                          int32_t parts_dtype, void* out, float* lse_out, int32_t out_dtype,
+                          int64_t B, int64_t H, int64_t S, int64_t D, void* stream) {
+  const int pes = elt_size(parts_dtype), oes = elt_size(out_dtype);
+  if (!pes || !oes) return fail(R3D_EUNSUPPORTED, "lse_merge: unknown dtype");
+  if (!o_parts || !lse_parts || !out) return fail(R3D_EINVAL, "lse_merge: NULL tensor pointer");
+  if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(out) || (lse_out && !aligned16(lse_out)))
+    return fail(R3D_EINVAL, "lse_merge: pointers must be 16-byte aligned");
+  if (n_parts < 1 || n_parts > 64) return fail(R3D_EINVAL, "lse_merge: n_parts=%d (1..64)", n_parts);
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return fail(R3D_EINVAL, "lse_merge: B, H, S, D must be > 0");
+  if (D % 8 != 0 || D > 256) return fail(R3D_EUNSUPPORTED, "lse_merge: D=%lld (multiple of 8, <= 256)", (long long)D);
+  int64_t rows, n_o, n_p;
+  if (!product(rows, {B, H, S}) || !product(n_o, {rows, D}) || !product(n_p, {n_o, (int64_t)n_parts}) ||
+      n_p > kMaxElems)
+    return fail(R3D_EINVAL, "lse_merge: tensor too large");
+  if (!launch_fits((rows * (D / 8) + 255) / 256, 256)) return fail(R3D_EINVAL, "lse_merge: too many rows for one launch");
+  if (overlap(out, n_o * oes, o_parts, n_p * pes) || overlap(out, n_o * oes, lse_parts, rows * n_parts * 4) ||
+      (lse_out && (overlap(lse_out, rows * 4, o_parts, n_p * pes) ||
+                   overlap(lse_out, rows * 4, lse_parts, rows * n_parts * 4) ||
+                   overlap(lse_out, rows * 4, out, n_o * oes))))
+    return fail(R3D_EINVAL, "lse_merge: an output overlaps an input or the other output");
+  return hip_status(r3d::launch_lse_merge(o_parts, lse_parts, n_parts, parts_dtype == R3D_BF16, out, lse_out,
+                                          out_dtype == R3D_BF16, rows, D, (hipStream_t)stream),
+                    "lse_merge");
+}
+
+}  // extern "C"

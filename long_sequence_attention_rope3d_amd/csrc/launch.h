@@ -1,0 +1,55 @@
+// Internal launcher interface between the C-ABI layer (capi.cpp) and the HIP
+// kernel files.  Not installed; every argument here has already been checked
+// by capi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace r3d {
+
+constexpr int kMaxSegs = 8;
+constexpr int kMaxPairs = 64;  // D/2 for D = 128
+
+// Rotary tables built on the host: per rotated pair p (0 .. D/2-1) its
+// frequency theta^(-2j/d_axis) (double) and its grid axis.
+struct RopeArgs {
+  double omega[kMaxPairs];
+  int8_t axis[kMaxPairs];  // 0 = t, 1 = h, 2 = w
+  int64_t grid_h, grid_w;
+  int32_t enabled;
+};
+
+struct SegArgs {
+  const void* src[kMaxSegs];
+  int64_t len[kMaxSegs];
+  int64_t off[kMaxSegs];
+  int32_t n;
+  int64_t S;  // sum of len
+};
+
+// rope3d_apply: [B, Nv, H, D] -> [B, Nv, H, D] (may be in place).
+hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t Nv, int64_t H,
+                         int64_t D, const RopeArgs& rope, hipStream_t stream);
+
+// joint_concat_permute: segments [B, S_i, H, D] -> [B, H, S, D]; rope.enabled
+// rotates segment 0.
+hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H,
+                          int64_t D, const RopeArgs& rope, hipStream_t stream);
+
+// attn_fwd, bf16 MFMA path (D = 64 or 128).
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                            int64_t kv_chunk, hipStream_t stream);
+
+// attn_fwd, fp32 path (D = 64 or 128).
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                           int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                           int64_t kv_chunk, hipStream_t stream);
+
+// lse_merge: parts [n, rows, D] + lse [n, rows] -> out [rows, D] (+ lse_out).
+hipError_t launch_lse_merge(const void* parts, const float* lse_parts, int32_t n, bool parts_bf16,
+                            void* out, float* lse_out, bool out_bf16, int64_t rows, int64_t D,
+                            hipStream_t stream);
+
+}  // namespace r3d

@@ -1,0 +1,194 @@
+// rope_permute.hip — 3-D rotary embedding and the joint concat +
+// sequence->head re-layout, as one HBM-bound kernel body.
+//
+// Operations ("Context Parallelism in vLLM Omni Neuron", §Self-Attention
+// with Context Parallelism: RoPE on query/key in [B, S, N, D], then
+// transpose(1, 2) to [B, N, S, D]; xDiT PR "Adds support for KV-cache and
+// joint tensors to USP method": joint tensors join the sequence inside
+// attention; the Ulysses input all-to-all is the multi-device form of the
+// re-layout):
+//   rope3d_apply         : [B, Nv, H, D] -> [B, Nv, H, D], video tokens rotated
+//   joint_concat_permute : segments [B, S_i, H, D] -> [B, H, S, D], optionally
+//                          rotating segment 0 (video) on the way through.
+//
+// Layout of the work.  A block owns kTok consecutive tokens of one batch row
+// and all H heads of them.  Per token, the cos/sin of its D/2 pair angles are
+// computed once into LDS and reused by all H heads (angles depend only on
+// the token).  Each thread then moves 16-byte chunks: a thread keeps one
+// (token, chunk) slot and walks the heads, so for a fixed head the block
+// reads one contiguous 256-byte row per token and writes kTok contiguous
+// rows of the [B, H, S, D] output — both sides are full-line, coalesced
+// accesses, and no LDS transpose is needed (the re-layout moves whole
+// D-rows).  Copies are bit-exact.  Angles, sin/cos and the rotation are
+// fp64 — the cos/sin table is per token and shared by all heads, so its cost
+// is small — followed by one round-to-nearest-even to the storage type: the
+// result is the correctly rounded rotation, also where x0 c - x1 s cancels
+// to a value far below |x| (an fp32 rotation is off by several bf16 ulps
+// there).
+#include "launch.h"
+
+namespace r3d {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = 8;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Correctly rounded binary64 -> bfloat16 (round to nearest, ties to even).
+// bfloat16 keeps 8 significant bits, so for |y| >= 2^-126 the binary64
+// significand is rounded at bit 45 by integer arithmetic; below 2^-126 the
+// spacing is fixed at 2^-133 and rint() on the scaled value rounds.  The
+// rounded value is exactly representable in binary32, whose upper half is
+// the bfloat16 pattern.
+__device__ __forceinline__ uint32_t f64_to_bf16(double y) {
+  uint64_t u = (uint64_t)__double_as_longlong(y);
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  double r;
+  if (a >= 0x7ff0000000000000ull) {
+    r = y;  // inf / nan
+  } else if (a >= 0x3810000000000000ull) {  // |y| >= 2^-126
+    u += 0x00001fffffffffffull + ((u >> 45) & 1u);
+    r = __longlong_as_double((long long)(u & ~0x00001fffffffffffull));
+  } else {
+    r = rint(y * 0x1p133) * 0x1p-133;
+  }
+  const uint32_t f = __float_as_uint((float)r);  // exact, or +-inf past the bf16 range
+  return ((f & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : (f >> 16);
+}
+
+// Rotates the pairs held in one 16-byte chunk.  Pair p of the row is
+// (x[2p], x[2p+1]); its (cos, sin) is cs[p].  The rotation is done in fp64
+// and rounded once to the storage type.
+template <bool BF16>
+__device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const double2* cs, int chunk) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const double2 c = cs[chunk * 4 + w];
+      const double x0 = (double)__uint_as_float(v[w] << 16);
+      const double x1 = (double)__uint_as_float(v[w] & 0xffff0000u);
+      v[w] = f64_to_bf16(x0 * c.x - x1 * c.y) | (f64_to_bf16(x0 * c.y + x1 * c.x) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const double2 c = cs[chunk * 2 + p];
+      const double x0 = (double)__uint_as_float(v[2 * p]), x1 = (double)__uint_as_float(v[2 * p + 1]);
+      v[2 * p] = __float_as_uint((float)(x0 * c.x - x1 * c.y));
+      v[2 * p + 1] = __float_as_uint((float)(x0 * c.y + x1 * c.x));
+    }
+  }
+  return v;
+}
+
+// PERMUTE = false: rope3d_apply layout (src and dst both [B, S, H, D], one
+//                  segment, every token rotated).
+// PERMUTE = true : joint concat into [B, H, S, D]; ROPE rotates segment 0.
+template <bool BF16, bool PERMUTE, bool ROPE>
+__global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, void* out,
+                                                                int H, int D, int64_t n_tb, RopeArgs rope) {
+  __shared__ double2 cs[kTok][kMaxPairs];
+  const int64_t b = (int64_t)blockIdx.x / n_tb;
+  const int64_t tok0 = ((int64_t)blockIdx.x - b * n_tb) * kTok;
+  const int64_t S = segs.S;
+  const int npairs = D / 2;
+  const int cpr = D * (BF16 ? 2 : 4) / 16;  // 16-byte chunks per row
+
+  if constexpr (ROPE) {
+    // Token n of the video segment sits at (t, h, w), n = (t*gh + h)*gw + w.
+    const int64_t nv = segs.len[0];
+    for (int e = threadIdx.x; e < kTok * npairs; e += kThreads) {
+      const int tl = e / npairs, p = e - tl * npairs;
+      const int64_t s = tok0 + tl;
+      double sn = 0.0, c = 1.0;
+      if (s < nv) {
+        const int64_t w = s % rope.grid_w;
+        const int64_t hw = s / rope.grid_w;
+        const int64_t h = hw % rope.grid_h;
+        const int64_t t = hw / rope.grid_h;
+        const int ax = rope.axis[p];
+        sincos((double)(ax == 0 ? t : (ax == 1 ? h : w)) * rope.omega[p], &sn, &c);
+      }
+      cs[tl][p] = make_double2(c, sn);
+    }
+    __syncthreads();
+  }
+
+  const int per_h = kTok * cpr;
+  if (per_h <= kThreads && kThreads % per_h == 0) {
+    // Each thread keeps one (token, chunk) slot and walks the heads.
+    const int slot = threadIdx.x % per_h;
+    const int tl = slot / cpr, chunk = slot - tl * cpr;
+    const int hstep = kThreads / per_h;
+    const int64_t s = tok0 + tl;
+    if (s >= S) return;
+    int seg = 0;
+    if constexpr (PERMUTE) {
+      while (seg + 1 < segs.n && s >= segs.off[seg + 1]) ++seg;
+    }
+    const int64_t ls = s - segs.off[seg];
+    const u32x4* src = reinterpret_cast<const u32x4*>(segs.src[seg]) + ((b * segs.len[seg] + ls) * H) * cpr + chunk;
+    u32x4* dst = reinterpret_cast<u32x4*>(out);
+    const bool rot = ROPE && seg == 0;
+#pragma unroll 4
+    for (int h = threadIdx.x / per_h; h < H; h += hstep) {
+      u32x4 v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
+      if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+      const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
+      __builtin_nontemporal_store(v, dst + o);
+    }
+  } else {
+    // Generic row widths (no RoPE: any D whose row is a multiple of 16 bytes).
+    const int64_t items = (int64_t)per_h * H;
+    for (int64_t idx = threadIdx.x; idx < items; idx += kThreads) {
+      const int h = (int)(idx / per_h);
+      const int slot = (int)(idx - (int64_t)h * per_h);
+      const int tl = slot / cpr, chunk = slot - tl * cpr;
+      const int64_t s = tok0 + tl;
+      if (s >= S) continue;
+      int seg = 0;
+      if constexpr (PERMUTE) {
+        while (seg + 1 < segs.n && s >= segs.off[seg + 1]) ++seg;
+      }
+      const int64_t ls = s - segs.off[seg];
+      u32x4 v = reinterpret_cast<const u32x4*>(segs.src[seg])[((b * segs.len[seg] + ls) * H + h) * cpr + chunk];
+      if (ROPE && seg == 0) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+      const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
+      reinterpret_cast<u32x4*>(out)[o] = v;
+    }
+  }
+}
+
+template <bool PERMUTE, bool ROPE>
+hipError_t launch_typed(bool bf16, const SegArgs& segs, void* out, int64_t B, int64_t H, int64_t D,
+                        const RopeArgs& rope, hipStream_t stream) {
+  const int64_t n_tb = (segs.S + kTok - 1) / kTok;  // token blocks per batch row
+  const unsigned grid = (unsigned)(n_tb * B);
+  if (bf16)
+    rope_permute_kernel<true, PERMUTE, ROPE><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
+  else
+    rope_permute_kernel<false, PERMUTE, ROPE><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t Nv, int64_t H, int64_t D,
+                         const RopeArgs& rope, hipStream_t stream) {
+  SegArgs segs{};
+  segs.src[0] = x;
+  segs.len[0] = Nv;
+  segs.off[0] = 0;
+  segs.n = 1;
+  segs.S = Nv;
+  return launch_typed<false, true>(bf16, segs, y, B, H, D, rope, stream);
+}
+
+hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H, int64_t D,
+                          const RopeArgs& rope, hipStream_t stream) {
+  if (rope.enabled) return launch_typed<true, true>(bf16, segs, out, B, H, D, rope, stream);
+  return launch_typed<true, false>(bf16, segs, out, B, H, D, rope, stream);
+}
+
+}  // namespace r3d

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/*.h (and nothing else), and rejects bad arguments on
+the host before anything is launched.
+
+The error-path calls pass fake, aligned, never-dereferenced addresses: every
+case below fails validation, which happens before any HIP call.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_sequence_attention_rope3d_amd as r3d
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = ctypes.CDLL(r3d.library_path())
+
+
+def _declared():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names += re.findall(r"R3D_API\s+[\w\s\*]+?\b(r3d_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd",
+                                  "r3d_lse_merge", "r3d_last_error", "r3d_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", r3d.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(LIB, name) is not None
+    ours = {n for n in exported if n.startswith("r3d_")}
+    assert ours == set(_declared())
+
+
+def test_version_string():
+    LIB.r3d_version.restype = ctypes.c_char_p
+    assert b"gfx950" in LIB.r3d_version()
+
+
+# ---------------------------------------------------------------------------------------------
+# Host-side validation (no launch happens in any of these)
+# ---------------------------------------------------------------------------------------------
+P = ctypes.c_void_p
+I32, I64 = ctypes.c_int32, ctypes.c_int64
+F = ctypes.c_float
+LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P]
+LIB.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, P, P]
+LIB.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64, P, P]
+LIB.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
+LIB.r3d_last_error.restype = ctypes.c_char_p
+
+A, B_, C, O, L_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _attn(**kw):
+    a = dict(q=A, k=B_, v=C, out=O, lse=L_, B=1, H=2, Sq=64, Skv=64, D=128, scale=0.125,
+             kv_chunk=0, dtype=1)
+    a.update(kw)
+    return LIB.r3d_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Sq"],
+                            a["Skv"], a["D"], a["scale"], a["kv_chunk"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(D=96), -2, "D=96"),
+    (dict(dtype=7), -2, "dtype"),
+    (dict(q=None), -1, "NULL"),
+    (dict(k=B_ + 8), -1, "aligned"),
+    (dict(Sq=0), -1, "> 0"),
+    (dict(Skv=-3), -1, "> 0"),
+    (dict(kv_chunk=-1), -1, "kv_chunk"),
+    (dict(scale=float("nan")), -1, "finite"),
+    (dict(scale=float("inf")), -1, "finite"),
+    (dict(out=A), -1, "overlaps"),
+    (dict(lse=O + 1024), -1, "overlaps"),
+    (dict(B=1 << 40, H=1 << 20), -1, "too large"),
+])
+def test_attn_fwd_rejects(kw, status, needle):
+    assert _attn(**kw) == status
+    assert needle in LIB.r3d_last_error().decode()
+
+
+class Rope(ctypes.Structure):
+    _fields_ = [("grid_t", I64), ("grid_h", I64), ("grid_w", I64), ("d_t", I32), ("d_h", I32),
+                ("d_w", I32), ("theta", ctypes.c_double)]
+
+
+@pytest.mark.parametrize("rope,Nv,D,status,needle", [
+    (Rope(2, 8, 15, 16, 24, 24, 1e4), 241, 64, -1, "grid product"),
+    (Rope(2, 8, 15, 16, 24, 26, 1e4), 240, 64, -1, "sum to D"),
+    (Rope(2, 8, 15, 15, 25, 24, 1e4), 240, 64, -1, "even"),
+    (Rope(2, 8, 15, 16, 24, 24, -1.0), 240, 64, -1, "theta"),
+    (Rope(0, 8, 15, 16, 24, 24, 1e4), 0, 64, -1, "> 0"),
+    (Rope(2, 8, 15, 32, 48, 16, 1e4), 240, 96, -2, "D=96"),
+])
+def test_rope3d_apply_rejects(rope, Nv, D, status, needle):
+    assert LIB.r3d_rope3d_apply(A, O, 1, 1, Nv, 2, D, ctypes.byref(rope), None) == status
+    assert needle in LIB.r3d_last_error().decode()
+
+
+def test_rope3d_apply_rejects_partial_overlap_and_null_desc():
+    r = Rope(2, 8, 15, 16, 24, 24, 1e4)
+    assert LIB.r3d_rope3d_apply(A, A + 64, 1, 1, 240, 2, 64, ctypes.byref(r), None) == -1
+    assert "overlap" in LIB.r3d_last_error().decode()
+    assert LIB.r3d_rope3d_apply(A, O, 1, 1, 240, 2, 64, None, None) == -1
+    assert "NULL" in LIB.r3d_last_error().decode()
+
+
+def _perm(ptrs, lens, out=O, D=128, dtype=1, rope=None):
+    arr = (P * len(ptrs))(*ptrs)
+    ln = (I64 * len(lens))(*lens)
+    return LIB.r3d_joint_concat_permute(ctypes.cast(arr, P), ctypes.cast(ln, P), len(ptrs), out,
+                                        dtype, 1, 2, D, ctypes.byref(rope) if rope else None, None)
+
+
+def test_permute_rejects():
+    assert _perm([A, B_], [10, -1]) == -1
+    assert _perm([A, None], [10, 5]) == -1 and "segment 1" in LIB.r3d_last_error().decode()
+    assert _perm([A], [0]) == -1 and "is 0" in LIB.r3d_last_error().decode()
+    assert _perm([A, B_], [10, 5], out=A + 256) == -1 and "overlaps" in LIB.r3d_last_error().decode()
+    assert _perm([A], [10], D=12) == -2          # 24-byte rows
+    assert _perm([A] * 9, [1] * 9) == -1         # too many segments
+    assert _perm([A], [240], D=64, rope=Rope(2, 8, 14, 16, 24, 24, 1e4)) == -1
+    assert _perm([A], [240], D=48, dtype=1, rope=Rope(2, 8, 15, 16, 16, 16, 1e4)) == -2
+
+
+def test_lse_merge_rejects():
+    def call(n=2, D=128, pdt=0, odt=1, out=O, lse_out=L_):
+        return LIB.r3d_lse_merge(A, B_, n, pdt, out, lse_out, odt, 1, 2, 64, D, None)
+    assert call(n=0) == -1
+    assert call(n=65) == -1
+    assert call(D=12) == -2
+    assert call(pdt=3) == -2
+    assert call(out=A + 4096) == -1 and "overlap" in LIB.r3d_last_error().decode()
+    assert call(lse_out=O + 16) == -1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 240, 2, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        r3d.rope3d_apply(x, (2, 8, 15), (16, 24, 24))
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        r3d.attn_fwd(q, q, q)

@@ -64,25 +64,24 @@ def digest(t: torch.Tensor) -> str:
     return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
 
 
-def sample_rows(w: Workload, n_random: int = 256, kv_tile: int = 64, seed_offset: int = 0,
-                heads=None) -> np.ndarray:
+def sample_rows(w: Workload, n_random: int = 16, seed_offset: int = 0, heads=None) -> np.ndarray:
     """Query rows for row-sampled parity at full size, as flat (b*H + h)*S + i.
 
-    Per head: the first and last video tokens, every joint token (capped at 64
-    per segment, evenly spread), rows at key-tile and chunk boundaries, the
-    last row, and ``n_random`` seeded random rows."""
+    Per head: the first and last video token, the first, middle and last
+    token of each joint segment, the rows on both sides of every kv_chunk
+    boundary (kv_chunk 0: every 1024th row), the last row, and ``n_random``
+    seeded random rows."""
     rng = np.random.default_rng(w.seed + 1000 + seed_offset)
     S = w.S
     base = {0, w.Nv - 1, S - 1}
     offs = np.cumsum((0,) + w.seg_lens)
     for i in range(1, len(w.seg_lens)):
         lo, hi = int(offs[i]), int(offs[i + 1])
-        base.update(np.linspace(lo, hi - 1, num=min(64, hi - lo), dtype=np.int64).tolist())
-    step = w.kv_chunk if w.kv_chunk > 0 else 1024
-    for b in range(0, S, step):
-        base.update({b, max(b - 1, 0)})
-    for b in range(0, S, 128 * 64):
-        base.update({b, min(b + kv_tile, S - 1)})
+        if hi > lo:
+            base.update({lo, (lo + hi) // 2, hi - 1})
+    step = w.kv_chunk if 0 < w.kv_chunk < S else 1024
+    for b in range(step, S, step):
+        base.update({b - 1, b})
     rows = []
     heads = range(w.H) if heads is None else heads
     for b in range(w.B):
