@@ -48,7 +48,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
   if (a >= 0x7ff0000000000000ull) {
     r = y;  // inf / nan
   } else if (a >= 0x3810000000000000ull) {  // |y| >= 2^-126
-    u += 0x00001fffffffffffull + ((u >> 45) & 1u);
+    u += 0x00000fffffffffffull + ((u >> 45) & 1u);
     r = __longlong_as_double((long long)(u & ~0x00001fffffffffffull));
   } else {
     r = rint(y * 0x1p133) * 0x1p-133;
