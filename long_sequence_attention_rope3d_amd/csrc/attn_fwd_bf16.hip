@@ -6,41 +6,53 @@
 // while the sequence is split).  Keys are visited in chunks of kv_chunk keys,
 // the single-device form of ring attention's one-K/V-shard-per-round loop
 // (§Ring attention):
-//   * inside a chunk: online softmax over key tiles of kBN keys (running max
-//     m, running sum l, accumulator acc rescaled by 2^(m_old - m_new));
+//   * inside a chunk: online softmax over 32-key steps (running max m,
+//     running sum l, accumulator acc rescaled by 2^(m_old - m_new));
 //   * at the end of a chunk: O_c = acc / l, lse_c = m + log2 l is merged into
 //     the running result (O, L) by the explicit log-sum-exp rule
 //       L' = log2(2^L + 2^lse_c),  O = O 2^(L - L') + O_c 2^(lse_c - L'),
 //     in registers; nothing partial is written to memory (§Memory and Compute
 //     Benefits: the split keeps full attention quality).
-// The softmax runs in the log2 domain: logits are pre-multiplied by
-// c = scale * log2(e) inside one FMA, so p = 2^(s*c - m).
+// The softmax runs in the log2 domain: logits are multiplied by
+// c = |scale| * log2(e) inside one FMA, so p = 2^(s*c - m).
 //
 // Mapping onto CDNA4
 // ------------------
-// * Block = 4 waves, 128 query rows (32 per wave); grid = B*H*ceil(Sq/128)
-//   blocks, re-numbered so that consecutive tiles of one head land on the
-//   same XCD (hardware hands block i to XCD i % 8), so the 32 CUs of an XCD
-//   stream the same K/V and share it through that XCD's L2.
-// * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows (from LDS), B = Q^T
-//   (kept in VGPRs for the whole block).  The 32x32 accumulator then holds,
-//   in lane l, 16 keys of query column l%32 — so each lane owns one query row
-//   and the row max / row sum need only in-lane work plus one exchange with
-//   lane l^32.
+// * Block = 8 waves = 256 query rows (32 per wave), i.e. two waves per SIMD:
+//   while one wave of a SIMD runs its softmax on the VALU the other keeps the
+//   matrix core busy (a single wave per SIMD issues VALU at half rate and
+//   stalls on its own MFMA chains).  That caps a wave at 256 registers.
+// * Grid = B*H*ceil(Sq/256) blocks, re-numbered so consecutive query tiles of
+//   one head land on the same XCD (hardware hands block i to XCD i % 8): the
+//   CUs of an XCD stream the same K/V and share it in that XCD's L2.
+// * K/V tiles of 64 keys are double-buffered in LDS in row-major [key][d]
+//   layout, 16-byte chunks XOR-swizzled per row so that the MFMA operand
+//   reads below hit distinct banks.  The next tile is fetched into registers
+//   (coalesced 16-byte loads) while the current one is consumed.
+// * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows (ds_read_b128),
+//   B = Q^T (kept in VGPRs for the whole block).  The accumulator holds, in
+//   lane l, 16 keys of query column l%32, so each lane owns one query row:
+//   the row max needs one v_permlane32_swap, the row sum none until the end
+//   of a chunk.
 // * K rows are fed to the MFMA in the permuted order pi (bits 2 and 3 of the
-//   row index swapped) so that accumulator element i of lane-half hf holds
-//   tile key 16*(i/8) + 8*hf + i%8: eight consecutive keys per half, exactly
-//   the B-operand fragment of the PV product.  P therefore goes from the
-//   S^T accumulator to the PV MFMA in registers (fp32 -> bf16 packed
-//   convert), with no LDS round trip.
-// * O^T = V^T P^T with the same MFMA: A = V^T (V stored transposed in LDS,
-//   so a lane's 8 keys are one 16-byte read), B = P^T.  The O^T accumulator
-//   again holds one query per lane, so the per-row rescale and the chunk
-//   merge are per-lane scalars.
-// * K and V^T tiles are double-buffered in LDS; the next tile's global loads
-//   are issued before the current tile's MFMAs and written to the other LDS
-//   buffer afterwards (one barrier per tile).  Rows are padded by 16 bytes so
-//   the 16-byte MFMA operand reads of a wave spread over all LDS banks.
+//   row index swapped) so accumulator element i of lane-half hf holds key
+//   16*(i/8) + 8*hf + i%8: eight consecutive keys per half — exactly the
+//   B-operand fragment of the PV product, so P goes from the S^T accumulator
+//   to the PV MFMA in registers (packed fp32 -> bf16 convert).
+// * O^T = V^T P^T: A = V^T, read from the row-major V tile with
+//   ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i%4
+//   of the rows addressed by lanes 4k + i/4, k = 0..3 — a 4x16 transpose of
+//   b16 values), two reads per 8-key fragment.  The O^T accumulator again
+//   holds one query per lane, so rescales and the chunk merge are per-lane
+//   scalars.
+// * Lazy rescale: the running max is only raised when a step's max exceeds
+//   it by more than kTau (log2 units); otherwise p = 2^(s*c - m) <= 2^kTau and
+//   acc keeps its scale.  The result is unchanged (the same m scales both
+//   acc and l); most steps skip the 64-register rescale of acc.
+// * The row sum l adds the fp32 p before their bf16 rounding for the PV
+//   product, so lse keeps fp32 accuracy.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace r3d {
@@ -50,25 +62,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per block
-constexpr int kBN = 64;           // keys per tile
+constexpr int kBN = 64;           // keys per LDS tile
 constexpr int kXcds = 8;
+constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
 template <int D>
 struct Geom {
-  static constexpr int kSteps = D / 16;                 // MFMA k-steps of Q K^T
-  static constexpr int kDBlk = D / 32;                  // 32-wide d blocks of O^T
-  static constexpr int kKRow = D + 8;                   // K tile row, elements (padded)
-  static constexpr int kVRow = kBN + 8;                 // V^T tile row, elements (padded)
-  static constexpr int kKElems = kBN * kKRow;
-  static constexpr int kVElems = D * kVRow;
-  static constexpr int kCpr = D / 8;                    // 16-byte chunks per K/V row
-  static constexpr int kKLoads = kBN * kCpr / kThreads; // 16-byte K loads per thread
-  static constexpr int kVItems = (kBN / 4) * (D / 8);   // 4-key x 8-d V items per tile
+  static constexpr int kSteps = D / 16;               // MFMA k-steps of Q K^T
+  static constexpr int kDBlk = D / 32;                // 32-wide d blocks of O^T
+  static constexpr int kCpr = D / 8;                  // 16-byte chunks per K/V row
+  static constexpr int kTile = kBN * D;               // elements of one K or V tile
+  static constexpr int kDma = kBN * kCpr / 64;         // 1 KB DMA instructions per tensor per tile
+  static constexpr int kDmaPerWave = kDma / kWaves;
+  static_assert(kDmaPerWave >= 1 && kDma % kWaves == 0, "tile/waves mismatch");
 };
+
+// Per-row XOR swizzles of the 16-byte chunk index (see the bank notes above).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) | ((r & 8) >> 1)) & (Geom<D>::kCpr - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (Geom<D>::kCpr - 1); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -79,59 +98,64 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// x of this lane combined with x of lane l^32.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // MFMA row m of the S^T product reads tile key pi(m): bits 2 and 3 swapped.
 __device__ __forceinline__ int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D>
-struct Stage {
-  u32x4 k[Geom<D>::kKLoads];
-  u32x4 v[4];
+// Walks the key tiles in order: tiles of kBN keys inside chunks of `chunk`
+// keys (the last tile of a chunk may be short), advanced by additions only.
+struct TileCursor {
+  int64_t kv0;   // first key of the tile
+  int64_t cend;  // end of the tile's chunk
+  __device__ __forceinline__ int n() const { return (int)((kv0 + kBN < cend) ? kBN : cend - kv0); }
+  __device__ __forceinline__ void advance(int64_t chunk, int64_t Skv) {
+    kv0 += kBN;
+    if (kv0 >= cend) {
+      kv0 = cend;
+      cend = (cend + chunk < Skv) ? cend + chunk : Skv;
+    }
+  }
 };
 
-// Global -> registers for the tile of n (<= kBN) keys starting at kv0.
-// Rows past n are zero (their logits are masked; zero V keeps 0 * V finite).
-template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const uint16_t* __restrict__ kb,
-                                          const uint16_t* __restrict__ vb, int64_t kv0, int n, int tid) {
+// Direct global -> LDS copy of one K or V tile (n valid keys from kv0) into
+// `tile`, as kDma wave-instructions of 64 x 16 bytes.  global_load_lds_dwordx4
+// writes lane L's 16 bytes to (instruction base + 16*L), so the swizzle is
+// realised by choosing, per lane, which global chunk lands in its slot: slot
+// s = 64*m + L holds row s / kCpr, logical chunk (s % kCpr) ^ swz(row).  Rows
+// past n re-read the last valid row (in bounds); their logits are masked and
+// their p is exactly zero.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restrict__ src, int64_t kv0, int n,
+                                         int wave, int lane) {
   using G = Geom<D>;
 #pragma unroll
-  for (int r = 0; r < G::kKLoads; ++r) {
-    const int idx = tid + r * kThreads;
-    const int row = idx / G::kCpr, ch = idx % G::kCpr;
-    st.k[r] = row < n ? *reinterpret_cast<const u32x4*>(kb + (kv0 + row) * D + ch * 8) : u32x4{0, 0, 0, 0};
-  }
-  if (tid < G::kVItems) {
-    const int kg = tid / G::kCpr, dc = tid % G::kCpr;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 4 * kg + j;
-      st.v[j] = key < n ? *reinterpret_cast<const u32x4*>(vb + (kv0 + key) * D + dc * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    const int m = wave + kWaves * i;
+    const int slot = 64 * m + lane;
+    const int r = slot / G::kCpr;
+    const int cl = (slot % G::kCpr) ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    const int64_t row = kv0 + (r < n ? r : n - 1);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * D + cl * 8),
+                                     (__attribute__((address_space(3))) void*)(tile + m * 64 * 8), 16, 0, 0);
   }
 }
 
-// Registers -> LDS: K row-major [key][d]; V transposed [d][key] (4 keys x 8 d
-// per thread, written as eight 8-byte rows of 4 keys).
-template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& st, uint16_t* ks, uint16_t* vts, int tid) {
-  using G = Geom<D>;
-#pragma unroll
-  for (int r = 0; r < G::kKLoads; ++r) {
-    const int idx = tid + r * kThreads;
-    const int row = idx / G::kCpr, ch = idx % G::kCpr;
-    *reinterpret_cast<u32x4*>(ks + row * G::kKRow + ch * 8) = st.k[r];
-  }
-  if (tid < G::kVItems) {
-    const int kg = tid / G::kCpr, dc = tid % G::kCpr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1;
-      const int sh = (i & 1) * 16;
-      const uint32_t e0 = (st.v[0][w] >> sh) & 0xffffu, e1 = (st.v[1][w] >> sh) & 0xffffu;
-      const uint32_t e2 = (st.v[2][w] >> sh) & 0xffffu, e3 = (st.v[3][w] >> sh) & 0xffffu;
-      *reinterpret_cast<u32x2*>(vts + (dc * 8 + i) * G::kVRow + 4 * kg) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-    }
-  }
+// Wait until at most N of this wave's vector-memory operations (here: LDS
+// DMAs) are outstanding and all of its LDS reads have returned, then meet the
+// other waves at the barrier.  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int D>
@@ -140,10 +164,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, int64_t Sq, int64_t Skv, float c, uint32_t qsign,
     int64_t chunk, int n_qt, int n_blocks) {
   using G = Geom<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][G::kKElems];
-  __shared__ __attribute__((aligned(16))) uint16_t vts[2][G::kVElems];
+  // Three K/V stages as distinct objects, so the compiler can tell that the
+  // reads of one stage do not alias the DMA in flight into the others.
+  __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1_k[G::kTile], st1_v[G::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2_k[G::kTile], st2_v[G::kTile];
 
-  // Block -> (head, query tile): XCD x runs logical tiles [x*q + min(x, r), ...).
+  // Block -> (head, query tile): XCD x runs logical tiles [x*per + min(x, rem), ...).
   const int bid = blockIdx.x;
   const int per = n_blocks / kXcds, rem = n_blocks % kXcds;
   const int xcd = bid % kXcds, slot = bid / kXcds;
@@ -167,6 +194,28 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, x);
   }
 
+  // Per-lane byte offsets of the MFMA operand reads inside a tile; every
+  // other term of the address is a compile-time immediate.
+  //  K: row 32*h2 + pi(r32), chunk 2*s + hf (swizzled); the 32-row half h2 adds
+  //     32*kCpr*16 bytes (the swizzle of row and row+32 is the same).
+  //  V: row 16*sg + 4*rd + 8*hf + (lane&15)/4 (row terms other than the last
+  //     two are immediates; the swizzle depends on row&3 only), elements
+  //     32*b + 16*((lane>>4)&1) + 4*(lane&3) .. +3.
+  int k_base[G::kSteps];
+  {
+    const int row = key_of_row(r32);
+#pragma unroll
+    for (int s = 0; s < G::kSteps; ++s) k_base[s] = (row * G::kCpr + ((2 * s + hf) ^ swz_k<D>(row))) * 16;
+  }
+  int v_base[G::kDBlk];
+  {
+    const int row = 8 * hf + ((lane & 15) >> 2);
+    const int d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < G::kDBlk; ++b)
+      v_base[b] = (row * G::kCpr + (((32 * b + d) >> 3) ^ swz_v<D>(row))) * 16 + (d & 7) * 2;
+  }
+
   f32x16 oacc[G::kDBlk], orun[G::kDBlk];
 #pragma unroll
   for (int b = 0; b < G::kDBlk; ++b) {
@@ -174,129 +223,137 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     orun[b] = f32x16{};
   }
   float m_run = -INFINITY, l_run = 0.f, L = -INFINITY;
-  bool first_chunk = true;
 
-  const int krow0 = key_of_row(r32);
-  int64_t kv = 0;
-  int64_t chunk_end = chunk < Skv ? chunk : Skv;
-  Stage<D> st;
-  load_tile<D>(st, kb, vb, 0, (int)((chunk_end < kBN) ? chunk_end : kBN), tid);
-  store_tile<D>(st, ks[0], vts[0], tid);
-  __syncthreads();
-  int buf = 0;
+  const int64_t first_cend = chunk < Skv ? chunk : Skv;
+  // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
+  TileCursor pf{0, first_cend};
+  dma_tile<D, false>(st0_k, kb, pf.kv0, pf.n(), wave, lane);
+  dma_tile<D, true>(st0_v, vb, pf.kv0, pf.n(), wave, lane);
+  pf.advance(chunk, Skv);
+  if (pf.kv0 < Skv) {
+    dma_tile<D, false>(st1_k, kb, pf.kv0, pf.n(), wave, lane);
+    dma_tile<D, true>(st1_v, vb, pf.kv0, pf.n(), wave, lane);
+    pf.advance(chunk, Skv);
+  }
+  // Both prologue tiles target different LDS objects, so their DMAs may be
+  // issued in either order: wait for all of them once.
+  wait_vm_barrier<0>();
 
-  while (true) {
-    const int64_t tile_end = (kv + kBN < chunk_end) ? kv + kBN : chunk_end;
-    const int n = (int)(tile_end - kv);
-    int64_t nkv = tile_end, nchunk_end = chunk_end;
-    if (nkv == chunk_end) nchunk_end = (chunk_end + chunk < Skv) ? chunk_end + chunk : Skv;
-    const bool has_next = nkv < Skv;
-    if (has_next) {
-      const int64_t ne = (nkv + kBN < nchunk_end) ? nkv + kBN : nchunk_end;
-      load_tile<D>(st, kb, vb, nkv, (int)(ne - nkv), tid);
+  // One tile of n keys in stage S: prefetch the tile after next into stage
+  // (S+2)%3, consume stage S, then wait for the next tile (this wave's part of
+  // it) and meet at the barrier.
+  auto step = [&](int n, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    const bool issue = pf.kv0 < Skv;
+    if (issue) {
+      dma_tile<D, false>(S == 0 ? st2_k : S == 1 ? st0_k : st1_k, kb, pf.kv0, pf.n(), wave, lane);
+      dma_tile<D, true>(S == 0 ? st2_v : S == 1 ? st0_v : st1_v, vb, pf.kv0, pf.n(), wave, lane);
+      pf.advance(chunk, Skv);
     }
 
-    // ---- S^T = K Q^T over the tile (two 32-key blocks) ----
-    const uint16_t* kt = ks[buf];
-    f32x16 sacc[2];
+    const char* kt = reinterpret_cast<const char*>(S == 0 ? st0_k : S == 1 ? st1_k : st2_k);
+    char* vt = reinterpret_cast<char*>(S == 0 ? st0_v : S == 1 ? st1_v : st2_v);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x16{};
-      const uint16_t* kp = kt + (32 * kb2 + krow0) * G::kKRow + 8 * hf;
+    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key softmax steps per tile
+      if (32 * h2 >= n) break;        // wholly past the end of the chunk
+      // ---- S^T = K Q^T for 32 keys ----
+      f32x16 sacc = f32x16{};
 #pragma unroll
       for (int s = 0; s < G::kSteps; ++s)
-        sacc[kb2] = mfma(*reinterpret_cast<const bf16x8*>(kp + 16 * s), qf[s], sacc[kb2]);
-    }
+        sacc = mfma(*reinterpret_cast<const bf16x8*>(kt + k_base[s] + h2 * 32 * G::kCpr * 16), qf[s], sacc);
 
-    // ---- online softmax (log2 domain), one query row per lane ----
-    // element i of sacc[kb2] is tile key 32*kb2 + 16*(i/8) + 8*hf + i%8
-    if (n < kBN) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
+      const bool partial = n < 32 * (h2 + 1);
+      const int lim = n - 32 * h2 - 8 * hf;  // element i is valid iff 16*(i/8) + i%8 < lim
+      if (partial) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * kb2 + 16 * (i / 8) + 8 * hf + (i % 8) >= n) sacc[kb2][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on a chunk's first tile
-    float psum = 0.f;
-    float p[2][16];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[kb2][i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][i], c, -m_new));
-        psum += p[kb2][i];
+          if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = -INFINITY;
       }
-    if (n < kBN) {  // masked keys: exactly zero, also when c == 0
-      psum = 0.f;
+      float mx = sacc[0];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+      mx = max_halves(mx);
+      const float cand = mx * c;
+      const float m_use = (cand > m_run + kTau) ? cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 if kept, 0 on a chunk's first step
+      if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (32 * kb2 + 16 * (i / 8) + 8 * hf + (i % 8) >= n) p[kb2][i] = 0.f;
-          psum += p[kb2][i];
+        for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
+      }
+      m_run = m_use;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
+      if (partial) {  // masked keys: exactly zero, also when c == 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = 0.f;
+      }
+      // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
+      float ps = l_run * alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps += sacc[i];
+      u32x4 pw[2];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
+      l_run = ps;
+
+      // ---- O^T += V^T P^T: two 16-key steps ----
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[sl]);
+        const int sg = 2 * h2 + sl;
+#pragma unroll
+        for (int b = 0; b < G::kDBlk; ++b) {
+          char* vp = vt + v_base[b] + 16 * sg * G::kCpr * 16;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * G::kCpr * 16));
+          const s16x4 a4[2] = {lo, hi};
+          oacc[b] = mfma(__builtin_bit_cast(bf16x8, a4), pf, oacc[b]);
         }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T: four 16-key steps ----
-    const uint16_t* vt = vts[buf];
-#pragma unroll
-    for (int sg = 0; sg < 4; ++sg) {
-      const int kb2 = sg >> 1, base = 8 * (sg & 1);
-      u32x4 pw;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pw[w] = pack_bf16(p[kb2][base + 2 * w], p[kb2][base + 2 * w + 1]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int b = 0; b < G::kDBlk; ++b)
-        oacc[b] = mfma(*reinterpret_cast<const bf16x8*>(vt + (32 * b + r32) * G::kVRow + 16 * sg + 8 * hf), pf,
-                       oacc[b]);
-    }
-
-    if (has_next) store_tile<D>(st, ks[buf ^ 1], vts[buf ^ 1], tid);
-    __syncthreads();
-
-    // ---- end of a chunk: explicit log-sum-exp merge into (orun, L) ----
-    if (tile_end == chunk_end) {
-      const float l_tot = l_run + __shfl_xor(l_run, 32);
-      const float lse_c = m_run + log2f(l_tot);
-      if (first_chunk) {
-        const float inv = 1.0f / l_tot;
-#pragma unroll
-        for (int b = 0; b < G::kDBlk; ++b) orun[b] = oacc[b] * inv;
-        L = lse_c;
-        first_chunk = false;
-      } else {
-        const float hi = fmaxf(L, lse_c);
-        const float Ln = hi + log2f(exp2f(L - hi) + exp2f(lse_c - hi));
-        const float wa = exp2f(L - Ln);
-        const float wb = exp2f(lse_c - Ln) / l_tot;
-#pragma unroll
-        for (int b = 0; b < G::kDBlk; ++b) orun[b] = orun[b] * wa + oacc[b] * wb;
-        L = Ln;
       }
-#pragma unroll
-      for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
-      m_run = -INFINITY;
-      l_run = 0.f;
     }
-    if (!has_next) break;
-    kv = nkv;
-    chunk_end = nchunk_end;
-    buf ^= 1;
+
+
+    if (issue)
+      wait_vm_barrier<2 * G::kDmaPerWave>();
+    else
+      wait_vm_barrier<0>();
+
+  };
+
+  // Chunk c covers tiles [c*tpc, min((c+1)*tpc, T)).  Inside a chunk the
+  // online softmax starts from m = -inf: the first step's alpha = 0 clears acc
+  // and l.  After the chunk, its partial (O_c = acc/l, lse_c = m + log2 l) is
+  // merged into (orun, L); with L = -inf initially the first merge gives
+  // weight 0 to orun, so no chunk is special.
+  int stage = 0;
+  for (int64_t c0 = 0; c0 < Skv; c0 += chunk) {
+    const int64_t c1 = (c0 + chunk < Skv) ? c0 + chunk : Skv;
+    m_run = -INFINITY;
+    for (int64_t kv0 = c0; kv0 < c1; kv0 += kBN) {
+      const int n = (int)((kv0 + kBN < c1) ? kBN : c1 - kv0);
+      if (stage == 0) {
+        step(n, std::integral_constant<int, 0>{});
+        stage = 1;
+      } else if (stage == 1) {
+        step(n, std::integral_constant<int, 1>{});
+        stage = 2;
+      } else {
+        step(n, std::integral_constant<int, 2>{});
+        stage = 0;
+      }
+    }
+    // ---- end of a chunk: explicit log-sum-exp merge into (orun, L) ----
+    const float l_tot = sum_halves(l_run);
+    const float lse_c = m_run + log2f(l_tot);
+    const float hi = fmaxf(L, lse_c);
+    const float Ln = hi + log2f(exp2f(L - hi) + exp2f(lse_c - hi));
+    const float wa = exp2f(L - Ln);
+    const float wb = exp2f(lse_c - Ln) / l_tot;
+#pragma unroll
+    for (int b = 0; b < G::kDBlk; ++b) orun[b] = orun[b] * wa + oacc[b] * wb;
+    L = Ln;
   }
 
   // ---- epilogue: out (bf16, RNE) and lse (natural log) ----
