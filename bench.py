@@ -87,7 +87,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pro-clip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072)
+    ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--no-kernels", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
