@@ -25,10 +25,12 @@
 // * Grid = B*H*ceil(Sq/256) blocks, re-numbered so consecutive query tiles of
 //   one head land on the same XCD (hardware hands block i to XCD i % 8): the
 //   CUs of an XCD stream the same K/V and share it in that XCD's L2.
-// * K/V tiles of 64 keys are double-buffered in LDS in row-major [key][d]
-//   layout, 16-byte chunks XOR-swizzled per row so that the MFMA operand
-//   reads below hit distinct banks.  The next tile is fetched into registers
-//   (coalesced 16-byte loads) while the current one is consumed.
+// * K/V tiles of 64 keys are copied global -> LDS by DMA
+//   (global_load_lds_dwordx4) into three stage buffers, row-major [key][d],
+//   with the 16-byte chunks of every row XOR-swizzled so that the operand
+//   reads served in one LDS cycle (16 lanes x 16 B for K, a 16-lane
+//   transpose group for V) fall into distinct banks (choices measured with
+//   the LDS bank-conflict counter).
 // * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows (ds_read_b128),
 //   B = Q^T (kept in VGPRs for the whole block).  The accumulator holds, in
 //   lane l, 16 keys of query column l%32, so each lane owns one query row:
@@ -65,10 +67,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 8;
+// Block shape: kWaves waves of 32 query rows; kStages K/V stage buffers in
+// LDS (prefetch distance kStages - 1 tiles).
+#ifndef R3D_ATTN_WAVES
+#define R3D_ATTN_WAVES 8
+#endif
+#ifndef R3D_ATTN_STAGES
+#define R3D_ATTN_STAGES 3
+#endif
+constexpr int kWaves = R3D_ATTN_WAVES;
+constexpr int kStages = R3D_ATTN_STAGES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per block
-constexpr int kBN = 64;           // keys per LDS tile
+constexpr int kWavesPerSimd = 2;  // two waves per SIMD: from one block (8 waves) or two (4 waves)
+static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
+#ifndef R3D_ATTN_BN
+#define R3D_ATTN_BN 64
+#endif
+constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 constexpr int kXcds = 8;
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
@@ -85,17 +101,28 @@ struct Geom {
 
 // Per-row XOR swizzles of the 16-byte chunk index (see the bank notes above).
 template <int D>
-__device__ __forceinline__ int swz_k(int r) { return ((r & 3) | ((r & 8) >> 1)) & (Geom<D>::kCpr - 1); }
+__device__ __forceinline__ int swz_k(int r) {
+  // ds_read_b128 is served 16 lanes (256 bytes) per LDS cycle; the 16 lanes of
+  // a group read 16 different rows at the same logical chunk.
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 template <int D>
-__device__ __forceinline__ int swz_v(int r) { return (4 * (r & 3)) & (Geom<D>::kCpr - 1); }
+__device__ __forceinline__ int swz_v(int r) {
+  // ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive rows x 32 bytes.
+  return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+}
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // x of this lane combined with x of lane l^32.
@@ -159,7 +186,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ lse, int64_t Sq, int64_t Skv, float c, uint32_t qsign,
     int64_t chunk, int n_qt, int n_blocks) {
@@ -230,31 +257,35 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   dma_tile<D, false>(st0_k, kb, pf.kv0, pf.n(), wave, lane);
   dma_tile<D, true>(st0_v, vb, pf.kv0, pf.n(), wave, lane);
   pf.advance(chunk, Skv);
-  if (pf.kv0 < Skv) {
+  if (kStages == 3 && pf.kv0 < Skv) {
     dma_tile<D, false>(st1_k, kb, pf.kv0, pf.n(), wave, lane);
     dma_tile<D, true>(st1_v, vb, pf.kv0, pf.n(), wave, lane);
     pf.advance(chunk, Skv);
   }
-  // Both prologue tiles target different LDS objects, so their DMAs may be
+  // The prologue tiles target different LDS objects, so their DMAs may be
   // issued in either order: wait for all of them once.
   wait_vm_barrier<0>();
 
   // One tile of n keys in stage S: prefetch the tile after next into stage
   // (S+2)%3, consume stage S, then wait for the next tile (this wave's part of
   // it) and meet at the barrier.
-  auto step = [&](int n, auto stage) {
+  TileCursor cur{0, first_cend};  // the tile being consumed
+  auto step = [&](auto stage) {
     constexpr int S = decltype(stage)::value;
+    const int n = cur.n();
+    const bool chunk_done = cur.kv0 + n == cur.cend;
     const bool issue = pf.kv0 < Skv;
     if (issue) {
-      dma_tile<D, false>(S == 0 ? st2_k : S == 1 ? st0_k : st1_k, kb, pf.kv0, pf.n(), wave, lane);
-      dma_tile<D, true>(S == 0 ? st2_v : S == 1 ? st0_v : st1_v, vb, pf.kv0, pf.n(), wave, lane);
+      constexpr int P = (S + kStages - 1) % kStages;  // stage of the tile kStages-1 ahead
+      dma_tile<D, false>(P == 0 ? st0_k : P == 1 ? st1_k : st2_k, kb, pf.kv0, pf.n(), wave, lane);
+      dma_tile<D, true>(P == 0 ? st0_v : P == 1 ? st1_v : st2_v, vb, pf.kv0, pf.n(), wave, lane);
       pf.advance(chunk, Skv);
     }
 
     const char* kt = reinterpret_cast<const char*>(S == 0 ? st0_k : S == 1 ? st1_k : st2_k);
     char* vt = reinterpret_cast<char*>(S == 0 ? st0_v : S == 1 ? st1_v : st2_v);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {  // two 32-key softmax steps per tile
+    for (int h2 = 0; h2 < kBN / 32; ++h2) {  // 32-key softmax steps of the tile
       if (32 * h2 >= n) break;        // wholly past the end of the chunk
       // ---- S^T = K Q^T for 32 keys ----
       f32x16 sacc = f32x16{};
@@ -263,13 +294,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
         sacc = mfma(*reinterpret_cast<const bf16x8*>(kt + k_base[s] + h2 * 32 * G::kCpr * 16), qf[s], sacc);
 
       // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
-      const bool partial = n < 32 * (h2 + 1);
-      const int lim = n - 32 * h2 - 8 * hf;  // element i is valid iff 16*(i/8) + i%8 < lim
-      if (partial) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = -INFINITY;
-      }
+      // Keys past the end of a short tile hold copies of its last valid key
+      // (the DMA clamps the row), so they cannot raise the max; only their p
+      // is zeroed below.
       float mx = sacc[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
@@ -284,7 +311,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
       m_run = m_use;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
-      if (partial) {  // masked keys: exactly zero, also when c == 0
+      if (n < 32 * (h2 + 1)) {  // short tile: keys past its end get p = 0 exactly
+        const int lim = n - 32 * h2 - 8 * hf;  // element i is a real key iff 16*(i/8) + i%8 < lim
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = 0.f;
@@ -315,45 +343,41 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     }
 
 
-    if (issue)
-      wait_vm_barrier<2 * G::kDmaPerWave>();
+    if (kStages == 3 && issue)
+      wait_vm_barrier<2 * G::kDmaPerWave>();  // the tile just issued may stay in flight
     else
       wait_vm_barrier<0>();
 
+    // ---- end of a chunk: explicit log-sum-exp merge into (orun, L) ----
+    if (chunk_done) {
+      const float l_tot = sum_halves(l_run);
+      const float lse_c = m_run + log2f(l_tot);
+      const float hi = fmaxf(L, lse_c);
+      const float Ln = hi + log2f(exp2f(L - hi) + exp2f(lse_c - hi));
+      const float wa = exp2f(L - Ln);
+      const float wb = exp2f(lse_c - Ln) / l_tot;
+#pragma unroll
+      for (int b = 0; b < G::kDBlk; ++b) orun[b] = orun[b] * wa + oacc[b] * wb;
+      L = Ln;
+      m_run = -INFINITY;  // the next chunk starts afresh: its first alpha is 0
+    }
+    cur.advance(chunk, Skv);
   };
 
-  // Chunk c covers tiles [c*tpc, min((c+1)*tpc, T)).  Inside a chunk the
-  // online softmax starts from m = -inf: the first step's alpha = 0 clears acc
-  // and l.  After the chunk, its partial (O_c = acc/l, lse_c = m + log2 l) is
-  // merged into (orun, L); with L = -inf initially the first merge gives
-  // weight 0 to orun, so no chunk is special.
-  int stage = 0;
-  for (int64_t c0 = 0; c0 < Skv; c0 += chunk) {
-    const int64_t c1 = (c0 + chunk < Skv) ? c0 + chunk : Skv;
-    m_run = -INFINITY;
-    for (int64_t kv0 = c0; kv0 < c1; kv0 += kBN) {
-      const int n = (int)((kv0 + kBN < c1) ? kBN : c1 - kv0);
-      if (stage == 0) {
-        step(n, std::integral_constant<int, 0>{});
-        stage = 1;
-      } else if (stage == 1) {
-        step(n, std::integral_constant<int, 1>{});
-        stage = 2;
-      } else {
-        step(n, std::integral_constant<int, 2>{});
-        stage = 0;
-      }
+  // Tiles run through stages 0, 1, 2, 0, ... in a straight line; a chunk's
+  // last tile ends with the explicit merge of its partial (O_c = acc/l,
+  // lse_c = m + log2 l) into (orun, L).  Inside a chunk the online softmax
+  // starts from m = -inf: the first step's alpha = 0 clears acc and l.  With
+  // L = -inf initially the first merge gives orun weight 0.
+  for (;;) {
+    step(std::integral_constant<int, 0>{});
+    if (cur.kv0 >= Skv) break;
+    step(std::integral_constant<int, 1>{});
+    if (cur.kv0 >= Skv) break;
+    if constexpr (kStages == 3) {
+      step(std::integral_constant<int, 2>{});
+      if (cur.kv0 >= Skv) break;
     }
-    // ---- end of a chunk: explicit log-sum-exp merge into (orun, L) ----
-    const float l_tot = sum_halves(l_run);
-    const float lse_c = m_run + log2f(l_tot);
-    const float hi = fmaxf(L, lse_c);
-    const float Ln = hi + log2f(exp2f(L - hi) + exp2f(lse_c - hi));
-    const float wa = exp2f(L - Ln);
-    const float wb = exp2f(lse_c - Ln) / l_tot;
-#pragma unroll
-    for (int b = 0; b < G::kDBlk; ++b) orun[b] = orun[b] * wa + oacc[b] * wb;
-    L = Ln;
   }
 
   // ---- epilogue: out (bf16, RNE) and lse (natural log) ----
