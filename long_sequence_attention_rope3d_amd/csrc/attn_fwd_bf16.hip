@@ -25,8 +25,8 @@
 // * Grid = B*H*ceil(Sq/256) blocks, re-numbered so consecutive query tiles of
 //   one head land on the same XCD (hardware hands block i to XCD i % 8): the
 //   CUs of an XCD stream the same K/V and share it in that XCD's L2.
-// * K/V tiles of 64 keys are copied global -> LDS by DMA
-//   (global_load_lds_dwordx4) into three stage buffers, row-major [key][d],
+// * K/V tiles of kBN = 128 keys are copied global -> LDS by DMA
+//   (global_load_lds_dwordx4) into two stage buffers, row-major [key][d],
 //   with the 16-byte chunks of every row XOR-swizzled so that the operand
 //   reads served in one LDS cycle (16 lanes x 16 B for K, a 16-lane
 //   transpose group for V) fall into distinct banks (choices measured with
@@ -73,7 +73,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #define R3D_ATTN_WAVES 8
 #endif
 #ifndef R3D_ATTN_STAGES
-#define R3D_ATTN_STAGES 3
+#define R3D_ATTN_STAGES 2
 #endif
 constexpr int kWaves = R3D_ATTN_WAVES;
 constexpr int kStages = R3D_ATTN_STAGES;
@@ -82,7 +82,7 @@ constexpr int kBM = 32 * kWaves;  // query rows per block
 constexpr int kWavesPerSimd = 2;  // two waves per SIMD: from one block (8 waves) or two (4 waves)
 static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 #ifndef R3D_ATTN_BN
-#define R3D_ATTN_BN 64
+#define R3D_ATTN_BN 128
 #endif
 constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 constexpr int kXcds = 8;
@@ -155,11 +155,21 @@ struct TileCursor {
 
 // Direct global -> LDS copy of one K or V tile (n valid keys from kv0) into
 // `tile`, as kDma wave-instructions of 64 x 16 bytes.  global_load_lds_dwordx4
-// writes lane L's 16 bytes to (instruction base + 16*L), so the swizzle is
-// realised by choosing, per lane, which global chunk lands in its slot: slot
-// s = 64*m + L holds row s / kCpr, logical chunk (s % kCpr) ^ swz(row).  Rows
-// past n re-read the last valid row (in bounds); their logits are masked and
-// their p is exactly zero.
+// writes lane L's 16 bytes to (M0 + 16*L), so the swizzle is realised by
+// choosing, per lane, which global chunk lands in its slot: slot s = 64*m + L
+// holds row s / kCpr, logical chunk (s % kCpr) ^ swz(row).  Rows past n
+// re-read the last valid row (in bounds); their logits are masked and their p
+// is exactly zero.
+//
+// The copy is issued from inline assembly on purpose: the compiler's own
+// wait-count insertion cannot prove that the LDS reads of the stage being
+// consumed are independent of the copy in flight into another stage, and
+// puts a full vmcnt(0) wait after every prefetch, exposing the whole copy
+// latency on each tile.  Hidden from it, the copies are ordered only by the
+// explicit waits in wait_vm_barrier (every read of a stage follows the wait
+// + barrier that retire that stage's copies).  The compiler's own vmcnt
+// waits (the Q loads) only become stricter by the extra operations in the
+// counter.  One wait state separates the M0 write from the DMA.
 template <int D, bool IS_V>
 __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restrict__ src, int64_t kv0, int n,
                                          int wave, int lane) {
@@ -171,18 +181,26 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restr
     const int r = slot / G::kCpr;
     const int cl = (slot % G::kCpr) ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
     const int64_t row = kv0 + (r < n ? r : n - 1);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row * D + cl * 8),
-                                     (__attribute__((address_space(3))) void*)(tile + m * 64 * 8), 16, 0, 0);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + m * 64 * 8));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + row * D + cl * 8),
+                 "s"(lds)
+                 : "memory", "m0");
   }
 }
 
 // Wait until at most N of this wave's vector-memory operations (here: LDS
 // DMAs) are outstanding and all of its LDS reads have returned, then meet the
-// other waves at the barrier.  The memory clobber keeps the compiler from
-// moving memory accesses across it.
+// other waves at the barrier.  The empty asm with a memory clobber keeps
+// memory accesses from being moved across the barrier.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // s_waitcnt immediate: vmcnt[3:0] in bits 3:0, expcnt (7 = no wait) in
+  // 6:4, lgkmcnt (0) in 11:8, vmcnt[5:4] in 15:14.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 template <int D>
@@ -191,8 +209,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     uint16_t* __restrict__ out, float* __restrict__ lse, int64_t Sq, int64_t Skv, float c, uint32_t qsign,
     int64_t chunk, int n_qt, int n_blocks) {
   using G = Geom<D>;
-  // Three K/V stages as distinct objects, so the compiler can tell that the
-  // reads of one stage do not alias the DMA in flight into the others.
+  // K/V stage buffers (the third only with kStages == 3).
   __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t st1_k[G::kTile], st1_v[G::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t st2_k[G::kTile], st2_v[G::kTile];
