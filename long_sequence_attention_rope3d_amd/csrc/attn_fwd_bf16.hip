@@ -8,11 +8,16 @@
 // (§Ring attention):
 //   * inside a chunk: online softmax over 32-key steps (running max m,
 //     running sum l, accumulator acc rescaled by 2^(m_old - m_new));
-//   * at the end of a chunk: O_c = acc / l, lse_c = m + log2 l is merged into
-//     the running result (O, L) by the explicit log-sum-exp rule
-//       L' = log2(2^L + 2^lse_c),  O = O 2^(L - L') + O_c 2^(lse_c - L'),
-//     in registers; nothing partial is written to memory (§Memory and Compute
-//     Benefits: the split keeps full attention quality).
+//   * across chunks, the log-sum-exp merge of the chunk partial
+//     (O_c, lse_c) = (acc_c / l_c, m_c + log2 l_c) into the running result
+//       L' = log2(2^L + 2^lse_c),  O' = O 2^(L - L') + O_c 2^(lse_c - L'),
+//     done in the accumulator itself: at a chunk end acc is normalised to
+//     (O, L) = (acc / l, m + log2 l) and the next chunk starts from acc = O,
+//     m = L, l = 1, i.e. the running result enters as value O at weight 2^L.
+//     The chunk's online rescale then produces exactly O' and L' (the
+//     formula above with both weights over the common normaliser), without a
+//     second 64-register accumulator.  Nothing partial is written to memory
+//     (§Memory and Compute Benefits: the split keeps full attention quality).
 // The softmax runs in the log2 domain: logits are multiplied by
 // c = |scale| * log2(e) inside one FMA, so p = 2^(s*c - m).
 //
@@ -85,6 +90,7 @@ static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 #define R3D_ATTN_BN 128
 #endif
 constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
+constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
 
@@ -101,15 +107,28 @@ struct Geom {
 
 // Per-row XOR swizzles of the 16-byte chunk index (see the bank notes above).
 template <int D>
-__device__ __forceinline__ int swz_k(int r) {
+constexpr __device__ __host__ int swz_k(int r) {
   // ds_read_b128 is served 16 lanes (256 bytes) per LDS cycle; the 16 lanes of
   // a group read 16 different rows at the same logical chunk.
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 template <int D>
-__device__ __forceinline__ int swz_v(int r) {
+constexpr __device__ __host__ int swz_v(int r) {
   // ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive rows x 32 bytes.
   return D == 128 ? 4 * (r & 3) : 2 * (r & 3);
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_u32(const uint16_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// True if the swizzle of row r equals that of row r + step for every row of a tile.
+template <int D, bool IS_V>
+constexpr bool swz_periodic(int step) {
+  for (int r = 0; r < 256; ++r)
+    if ((IS_V ? swz_v<D>(r) : swz_k<D>(r)) != (IS_V ? swz_v<D>(r + step) : swz_k<D>(r + step))) return false;
+  return true;
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -153,13 +172,15 @@ struct TileCursor {
   }
 };
 
-// Direct global -> LDS copy of one K or V tile (n valid keys from kv0) into
-// `tile`, as kDma wave-instructions of 64 x 16 bytes.  global_load_lds_dwordx4
+// Direct global -> LDS copy of one K or V tile into the LDS bytes at
+// lds_tile, as kDma wave-instructions of 64 x 16 bytes; `src` points at the
+// tile's first key row and n of its rows are valid.  global_load_lds_dwordx4
 // writes lane L's 16 bytes to (M0 + 16*L), so the swizzle is realised by
 // choosing, per lane, which global chunk lands in its slot: slot s = 64*m + L
 // holds row s / kCpr, logical chunk (s % kCpr) ^ swz(row).  Rows past n
-// re-read the last valid row (in bounds); their logits are masked and their p
-// is exactly zero.
+// re-read the last valid row (in bounds); their logits are masked and their
+// p is exactly zero.  kFull: n == kBN, no clamp.  The global address is the
+// wave-uniform tile base (SGPRs) plus a 32-bit per-lane byte offset.
 //
 // The copy is issued from inline assembly on purpose: the compiler's own
 // wait-count insertion cannot prove that the LDS reads of the stage being
@@ -167,24 +188,40 @@ struct TileCursor {
 // puts a full vmcnt(0) wait after every prefetch, exposing the whole copy
 // latency on each tile.  Hidden from it, the copies are ordered only by the
 // explicit waits in wait_vm_barrier (every read of a stage follows the wait
-// + barrier that retire that stage's copies).  The compiler's own vmcnt
-// waits (the Q loads) only become stricter by the extra operations in the
-// counter.  One wait state separates the M0 write from the DMA.
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* __restrict__ src, int64_t kv0, int n,
-                                         int wave, int lane) {
+// + barrier that retire that stage's copies).  The compiler's own vmcnt waits
+// (the Q loads) only become stricter by the extra operations in the counter.
+// One wait state separates the M0 write from the DMA.
+template <int D, bool IS_V, bool kFull>
+__device__ __forceinline__ void dma_tile(uint32_t lds_tile, const uint16_t* src, int n, int wave, int lane) {
   using G = Geom<D>;
+  // Instruction i of a wave covers slots 64*(wave + kWaves*i) + [0, 64): rows
+  // r0 + kRowStep*i.  The swizzles depend on row bits that kRowStep leaves
+  // unchanged, so the chunk (and for full tiles the whole per-lane offset) is
+  // the same for every i; instruction i adds kRowStep rows (8 KB) to the
+  // wave-uniform global base and to M0.
+  constexpr int kRowStep = 64 * kWaves / G::kCpr;
+  static_assert(swz_periodic<D, IS_V>(kRowStep), "swizzle must be invariant under a step of kRowStep rows");
+  const int r0 = (64 * wave + lane) / G::kCpr;
+  const int cl = (lane % G::kCpr) ^ (IS_V ? swz_v<D>(r0) : swz_k<D>(r0));
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    const int m = wave + kWaves * i;
-    const int slot = 64 * m + lane;
-    const int r = slot / G::kCpr;
-    const int cl = (slot % G::kCpr) ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
-    const int64_t row = kv0 + (r < n ? r : n - 1);
-    const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(tile + m * 64 * 8));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src + row * D + cl * 8),
-                 "s"(lds)
+    // Full tile: base advanced by i*kRowStep rows, offset of row r0.  Short
+    // tile: base at the tile, offset of the clamped absolute row.  Either way
+    // the unsigned 32-bit offset is the in-bounds row's distance from base.
+    const int r = r0 + kRowStep * i;
+    const int row = kFull ? r0 : (r < n ? r : n - 1);
+    const uint32_t off = (uint32_t)(row * D + cl * 8) * 2u;
+    const uint16_t* const src_i = kFull ? src + (int64_t)kRowStep * i * D : src;
+    // Both are wave-uniform; readfirstlane pins them to SGPRs, which the
+    // asm operands require (the compiler would otherwise hand over a VGPR).
+    const uint64_t b64 = reinterpret_cast<uint64_t>(src_i);
+    // (readfirstlane returns int: go through uint32_t so nothing sign-extends.)
+    const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+    const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
+    const uint64_t base = (uint64_t)b_lo | ((uint64_t)b_hi << 32);
+    const uint32_t lds =
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_tile + (uint32_t)((wave + kWaves * i) * 64 * 16)));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
   }
 }
@@ -222,7 +259,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   const int64_t bh = logical / n_qt;
   const int qt = logical - (int)bh * n_qt;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31, hf = lane >> 5;
   const int64_t qrow = (int64_t)qt * kBM + wave * 32 + r32;
   const uint16_t* kb = k + bh * Skv * D;
@@ -260,25 +298,34 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       v_base[b] = (row * G::kCpr + (((32 * b + d) >> 3) ^ swz_v<D>(row))) * 16 + (d & 7) * 2;
   }
 
-  f32x16 oacc[G::kDBlk], orun[G::kDBlk];
+  f32x16 oacc[G::kDBlk];
 #pragma unroll
-  for (int b = 0; b < G::kDBlk; ++b) {
-    oacc[b] = f32x16{};
-    orun[b] = f32x16{};
-  }
-  float m_run = -INFINITY, l_run = 0.f, L = -INFINITY;
+  for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
+  // Running state: acc (oacc), max m and per-lane partial sum l, log2 domain.
+  float m_run = -INFINITY, l_run = 0.f;
 
   const int64_t first_cend = chunk < Skv ? chunk : Skv;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
   TileCursor pf{0, first_cend};
-  dma_tile<D, false>(st0_k, kb, pf.kv0, pf.n(), wave, lane);
-  dma_tile<D, true>(st0_v, vb, pf.kv0, pf.n(), wave, lane);
-  pf.advance(chunk, Skv);
-  if (kStages == 3 && pf.kv0 < Skv) {
-    dma_tile<D, false>(st1_k, kb, pf.kv0, pf.n(), wave, lane);
-    dma_tile<D, true>(st1_v, vb, pf.kv0, pf.n(), wave, lane);
+  // Copy tile pf into stage P (K and V), then advance pf.
+  auto copy = [&](auto stage) {
+    constexpr int P = decltype(stage)::value;
+    const int n = pf.n();
+    const uint32_t lk = lds_u32(P == 0 ? st0_k : P == 1 ? st1_k : st2_k);
+    const uint32_t lv = lds_u32(P == 0 ? st0_v : P == 1 ? st1_v : st2_v);
+    const uint16_t* ks = kb + pf.kv0 * D;
+    const uint16_t* vs = vb + pf.kv0 * D;
+    if (n == kBN) {
+      dma_tile<D, false, true>(lk, ks, n, wave, lane);
+      dma_tile<D, true, true>(lv, vs, n, wave, lane);
+    } else {
+      dma_tile<D, false, false>(lk, ks, n, wave, lane);
+      dma_tile<D, true, false>(lv, vs, n, wave, lane);
+    }
     pf.advance(chunk, Skv);
-  }
+  };
+  copy(std::integral_constant<int, 0>{});
+  if (kStages == 3 && pf.kv0 < Skv) copy(std::integral_constant<int, 1>{});
   // The prologue tiles target different LDS objects, so their DMAs may be
   // issued in either order: wait for all of them once.
   wait_vm_barrier<0>();
@@ -292,28 +339,45 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const int n = cur.n();
     const bool chunk_done = cur.kv0 + n == cur.cend;
     const bool issue = pf.kv0 < Skv;
-    if (issue) {
-      constexpr int P = (S + kStages - 1) % kStages;  // stage of the tile kStages-1 ahead
-      dma_tile<D, false>(P == 0 ? st0_k : P == 1 ? st1_k : st2_k, kb, pf.kv0, pf.n(), wave, lane);
-      dma_tile<D, true>(P == 0 ? st0_v : P == 1 ? st1_v : st2_v, vb, pf.kv0, pf.n(), wave, lane);
-      pf.advance(chunk, Skv);
-    }
+    if (issue) copy(std::integral_constant<int, (S + kStages - 1) % kStages>{});  // the tile kStages-1 ahead
 
     const char* kt = reinterpret_cast<const char*>(S == 0 ? st0_k : S == 1 ? st1_k : st2_k);
     char* vt = reinterpret_cast<char*>(S == 0 ? st0_v : S == 1 ? st1_v : st2_v);
+    // 32-key steps, software-pipelined inside the tile: step h's S^T = K Q^T
+    // is issued before step h-1's PV product, so the matrix core runs that PV
+    // while the same wave computes step h's softmax on the VALU.  In a short
+    // tile, steps wholly past n still run: their keys are copies of the last
+    // valid key (the DMA clamps the row), which cannot raise the max, and all
+    // their p are zeroed.
+    u32x4 pw[2];  // P of the step whose PV is pending, as bf16 pairs
 #pragma unroll
-    for (int h2 = 0; h2 < kBN / 32; ++h2) {  // 32-key softmax steps of the tile
-      if (32 * h2 >= n) break;        // wholly past the end of the chunk
-      // ---- S^T = K Q^T for 32 keys ----
+    for (int h2 = 0; h2 <= kSub; ++h2) {
       f32x16 sacc = f32x16{};
+      if (h2 < kSub) {
+        // ---- S^T = K Q^T for keys [32*h2, 32*h2 + 32) ----
 #pragma unroll
-      for (int s = 0; s < G::kSteps; ++s)
-        sacc = mfma(*reinterpret_cast<const bf16x8*>(kt + k_base[s] + h2 * 32 * G::kCpr * 16), qf[s], sacc);
+        for (int s = 0; s < G::kSteps; ++s)
+          sacc = mfma(*reinterpret_cast<const bf16x8*>(kt + k_base[s] + h2 * 32 * G::kCpr * 16), qf[s], sacc);
+      }
+      if (h2 > 0) {
+        // ---- O^T += V^T P^T for step h2-1: two 16-key steps ----
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[sl]);
+          const int sg = 2 * (h2 - 1) + sl;
+#pragma unroll
+          for (int b = 0; b < G::kDBlk; ++b) {
+            char* vp = vt + v_base[b] + 16 * sg * G::kCpr * 16;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * G::kCpr * 16));
+            const s16x4 a4[2] = {lo, hi};
+            oacc[b] = mfma(__builtin_bit_cast(bf16x8, a4), pf, oacc[b]);
+          }
+        }
+      }
+      if (h2 == kSub) break;
 
       // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
-      // Keys past the end of a short tile hold copies of its last valid key
-      // (the DMA clamps the row), so they cannot raise the max; only their p
-      // is zeroed below.
       float mx = sacc[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
@@ -321,10 +385,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       const float cand = mx * c;
       const float m_use = (cand > m_run + kTau) ? cand : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 if kept, 0 on a chunk's first step
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
-      }
       m_run = m_use;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
@@ -338,54 +398,41 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       float ps = l_run * alpha;
 #pragma unroll
       for (int i = 0; i < 16; ++i) ps += sacc[i];
-      u32x4 pw[2];
+      l_run = ps;
 #pragma unroll
       for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
-      l_run = ps;
-
-      // ---- O^T += V^T P^T: two 16-key steps ----
+      // Rescale acc last: it already holds step h2-1's PV (issued above), and
+      // step h2's PV comes after.
+      if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[sl]);
-        const int sg = 2 * h2 + sl;
-#pragma unroll
-        for (int b = 0; b < G::kDBlk; ++b) {
-          char* vp = vt + v_base[b] + 16 * sg * G::kCpr * 16;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * G::kCpr * 16));
-          const s16x4 a4[2] = {lo, hi};
-          oacc[b] = mfma(__builtin_bit_cast(bf16x8, a4), pf, oacc[b]);
-        }
+        for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
       }
     }
-
 
     if (kStages == 3 && issue)
       wait_vm_barrier<2 * G::kDmaPerWave>();  // the tile just issued may stay in flight
     else
       wait_vm_barrier<0>();
 
-    // ---- end of a chunk: explicit log-sum-exp merge into (orun, L) ----
+    // ---- end of a chunk: log-sum-exp merge ----
+    // (acc, m, l) now describe the running result merged with this chunk:
+    // normalise to (O, L) = (acc / l, m + log2 l), and let the next chunk
+    // start from acc = O, m = L, l = 1 -- value O at weight 2^L.  The next
+    // chunk's online rescale then forms exactly O 2^(L - L') + O_c 2^(lse_c - L').
     if (chunk_done) {
       const float l_tot = sum_halves(l_run);
-      const float lse_c = m_run + log2f(l_tot);
-      const float hi = fmaxf(L, lse_c);
-      const float Ln = hi + log2f(exp2f(L - hi) + exp2f(lse_c - hi));
-      const float wa = exp2f(L - Ln);
-      const float wb = exp2f(lse_c - Ln) / l_tot;
+      const float inv = 1.0f / l_tot;
 #pragma unroll
-      for (int b = 0; b < G::kDBlk; ++b) orun[b] = orun[b] * wa + oacc[b] * wb;
-      L = Ln;
-      m_run = -INFINITY;  // the next chunk starts afresh: its first alpha is 0
+      for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
+      m_run += log2f(l_tot);
+      l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
     }
     cur.advance(chunk, Skv);
   };
 
-  // Tiles run through stages 0, 1, 2, 0, ... in a straight line; a chunk's
-  // last tile ends with the explicit merge of its partial (O_c = acc/l,
-  // lse_c = m + log2 l) into (orun, L).  Inside a chunk the online softmax
-  // starts from m = -inf: the first step's alpha = 0 clears acc and l.  With
-  // L = -inf initially the first merge gives orun weight 0.
+  // Tiles run through the stages in a straight line; a chunk's last tile ends
+  // with the merge.  The first chunk starts from m = -inf: its first step's
+  // alpha = 0 clears acc and l.
   for (;;) {
     step(std::integral_constant<int, 0>{});
     if (cur.kv0 >= Skv) break;
@@ -398,18 +445,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   }
 
   // ---- epilogue: out (bf16, RNE) and lse (natural log) ----
-  // orun[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
+  // The last tile closed a chunk, so acc = O and m = L (log2).
+  // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
   if (qrow < Sq) {
     uint16_t* op = out + (bh * Sq + qrow) * D;
 #pragma unroll
     for (int b = 0; b < G::kDBlk; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x2 w = u32x2{pack_bf16(orun[b][4 * g], orun[b][4 * g + 1]),
-                              pack_bf16(orun[b][4 * g + 2], orun[b][4 * g + 3])};
+        const u32x2 w = u32x2{pack_bf16(oacc[b][4 * g], oacc[b][4 * g + 1]),
+                              pack_bf16(oacc[b][4 * g + 2], oacc[b][4 * g + 3])};
         *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * hf) = w;
       }
-    if (lse && hf == 0) lse[bh * Sq + qrow] = L * 0.69314718055994530942f;
+    if (lse && hf == 0) lse[bh * Sq + qrow] = m_run * 0.69314718055994530942f;
   }
 }
 
