@@ -388,19 +388,27 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       m_run = m_use;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
-      if (n < 32 * (h2 + 1)) {  // short tile: keys past its end get p = 0 exactly
+      // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
+      const float l_base = l_run * alpha;
+      float ps = l_base;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps += sacc[i];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
+      if (n < 32 * (h2 + 1)) {
+        // Short tile (rare; kept out of the common block): keys past its end
+        // get p = 0 exactly; redo the sum and the packing.
         const int lim = n - 32 * h2 - 8 * hf;  // element i is a real key iff 16*(i/8) + i%8 < lim
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = 0.f;
+        ps = l_base;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps += sacc[i];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
       }
-      // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
-      float ps = l_run * alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ps += sacc[i];
       l_run = ps;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
       // Rescale acc last: it already holds step h2-1's PV (issued above), and
       // step h2's PV comes after.
       if (__ballot(alpha != 1.0f)) {
