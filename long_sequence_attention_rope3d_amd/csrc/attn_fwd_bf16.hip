@@ -23,11 +23,13 @@
 //
 // Mapping onto CDNA4
 // ------------------
-// * Block = 8 waves = 256 query rows (32 per wave), i.e. two waves per SIMD:
-//   while one wave of a SIMD runs its softmax on the VALU the other keeps the
-//   matrix core busy (a single wave per SIMD issues VALU at half rate and
-//   stalls on its own MFMA chains).  That caps a wave at 256 registers.
-// * Grid = B*H*ceil(Sq/256) blocks, re-numbered so consecutive query tiles of
+// * Block = 12 waves = 384 query rows (32 per wave), one block per CU, i.e.
+//   three waves per SIMD: while one wave of a SIMD runs its softmax on the
+//   VALU or waits on LDS, the others keep the matrix core busy.  That caps a
+//   wave at 168 registers (the kernel needs ~166 and spills nothing).  384
+//   also divides the 52608-token workload exactly, and 137 query tiles per
+//   head keep the last round of blocks on the CUs nearly full.
+// * Grid = B*H*ceil(Sq/384) blocks, re-numbered so consecutive query tiles of
 //   one head land on the same XCD (hardware hands block i to XCD i % 8): the
 //   CUs of an XCD stream the same K/V and share it in that XCD's L2.
 // * K/V tiles of kBN = 128 keys are copied global -> LDS by DMA
@@ -75,7 +77,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Block shape: kWaves waves of 32 query rows; kStages K/V stage buffers in
 // LDS (prefetch distance kStages - 1 tiles).
 #ifndef R3D_ATTN_WAVES
-#define R3D_ATTN_WAVES 8
+#define R3D_ATTN_WAVES 12
 #endif
 #ifndef R3D_ATTN_STAGES
 #define R3D_ATTN_STAGES 2
@@ -84,7 +86,8 @@ constexpr int kWaves = R3D_ATTN_WAVES;
 constexpr int kStages = R3D_ATTN_STAGES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per block
-constexpr int kWavesPerSimd = 2;  // two waves per SIMD: from one block (8 waves) or two (4 waves)
+constexpr int kWavesPerSimd = kWaves / 4;  // waves per SIMD (one block per CU)
+static_assert(kWaves % 4 == 0, "whole waves per SIMD");
 static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 #ifndef R3D_ATTN_BN
 #define R3D_ATTN_BN 128
@@ -101,8 +104,11 @@ struct Geom {
   static constexpr int kCpr = D / 8;                  // 16-byte chunks per K/V row
   static constexpr int kTile = kBN * D;               // elements of one K or V tile
   static constexpr int kDma = kBN * kCpr / 64;         // 1 KB DMA instructions per tensor per tile
-  static constexpr int kDmaPerWave = kDma / kWaves;
-  static_assert(kDmaPerWave >= 1 && kDma % kWaves == 0, "tile/waves mismatch");
+  static constexpr int kDmaPerWave = (kDma + kWaves - 1) / kWaves;  // the last may be partial
+  static_assert(kDma >= kWaves, "every wave copies");
+  // With a tile left in flight across the barrier (3 stages) every wave must
+  // issue the same number of copies for its vmcnt wait to cover the older tile.
+  static_assert(kStages == 2 || kDma % kWaves == 0, "uneven copy split needs 2 stages");
 };
 
 // Per-row XOR swizzles of the 16-byte chunk index (see the bank notes above).
@@ -205,6 +211,7 @@ __device__ __forceinline__ void dma_tile(uint32_t lds_tile, const uint16_t* src,
   const int cl = (lane % G::kCpr) ^ (IS_V ? swz_v<D>(r0) : swz_k<D>(r0));
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
+    if (G::kDma % kWaves != 0 && wave + kWaves * i >= G::kDma) break;  // wave-uniform
     // Full tile: base advanced by i*kRowStep rows, offset of row r0.  Short
     // tile: base at the tile, offset of the clamped absolute row.  Either way
     // the unsigned 32-bit offset is the in-bounds row's distance from base.
