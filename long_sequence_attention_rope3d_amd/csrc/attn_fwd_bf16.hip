@@ -391,15 +391,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       mx = max_halves(mx);
       const float cand = mx * c;
       const float m_use = (cand > m_run + kTau) ? cand : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 if kept, 0 on a chunk's first step
-      m_run = m_use;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
       // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
-      const float l_base = l_run * alpha;
-      float ps = l_base;
+      float ps = sacc[0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ps += sacc[i];
+      for (int i = 1; i < 16; ++i) ps += sacc[i];
 #pragma unroll
       for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
       if (n < 32 * (h2 + 1)) {
@@ -409,19 +406,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (16 * (i / 8) + (i % 8) >= lim) sacc[i] = 0.f;
-        ps = l_base;
+        ps = sacc[0];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ps += sacc[i];
+        for (int i = 1; i < 16; ++i) ps += sacc[i];
 #pragma unroll
         for (int w = 0; w < 8; ++w) pw[w >> 2][w & 3] = pack_bf16(sacc[2 * w], sacc[2 * w + 1]);
       }
-      l_run = ps;
-      // Rescale acc last: it already holds step h2-1's PV (issued above), and
-      // step h2's PV comes after.
-      if (__ballot(alpha != 1.0f)) {
+      // Rescale last, and only when some row's reference moved (alpha is 0 on
+      // a chunk's first step): acc already holds step h2-1's PV (issued above),
+      // and step h2's PV comes after.
+      if (__ballot(m_use != m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
       }
+      l_run += ps;
+      m_run = m_use;
     }
 
     if (kStages == 3 && issue)
