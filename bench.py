@@ -146,7 +146,7 @@ def main():
 
     kernels = {}
     if not args.no_kernels:
-        kernels = time_side_kernels(torch, r3d, w, segs, q, lse, rope, dev, stream)
+        kernels = time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream)
 
     traffic_bytes = _traffic_for_current_kernel()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
@@ -187,7 +187,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def time_side_kernels(torch, r3d, w, segs, q, lse, rope, dev, stream, reps: int = 5):
+def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps: int = 5):
     """HBM-bound entry points on this workload's shapes, as GB/s of
     algorithmic bytes (each input read once, each output written once)."""
     def timed(fn):
@@ -231,6 +231,15 @@ def time_side_kernels(torch, r3d, w, segs, q, lse, rope, dev, stream, reps: int 
     for kname, r in res.items():
         r["frac_hbm_peak"] = round(r["GBps"] / MI355X_HBM_GBPS, 4)
         log(f"{kname}: {r['ms']:.3f} ms, {r['GBps']:.0f} GB/s")
+    # attn_fwd writing its output token-major ([B,S,H,D], the inverse re-layout
+    # fused into the epilogue); same flops as the timed step's attn_fwd.
+    r3d.joint_concat_permute(segs["q"], rope, out=q)
+    obshd = torch.empty((w.B, w.S, w.H, w.D), dtype=q.dtype, device=dev)
+    ms = timed(lambda: r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk, out=obshd, lse=lse,
+                                    out_layout="bshd"))
+    res["attn_fwd_bshd"] = {"ms": round(ms, 4), "TFLOPs": round(w.attn_flops / (ms * 1e-3) / 1e12, 2)}
+    log(f"attn_fwd_bshd: {ms:.3f} ms, {res['attn_fwd_bshd']['TFLOPs']:.1f} TFLOP/s")
+    del obshd
     return res
 
 

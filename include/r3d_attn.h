@@ -133,6 +133,22 @@ R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
                          int64_t kv_chunk, int32_t dtype, void* stream);
 
 /*
+ * r3d_attn_fwd_bshd — r3d_attn_fwd with the output written token-major:
+ *   out : [B, Sq, H, D] (everything else, lse included, as in r3d_attn_fwd).
+ * This is the inverse of the [B, S, H, D] -> [B, H, S, D] re-layout done by
+ * r3d_joint_concat_permute, i.e. the local form of the Ulysses output
+ * all-to-all that returns the head-sharded result to sequence order (xDiT PR
+ * #586, USP: _ft_c_output_all_to_all(out)), and the token-major form that the
+ * output projection consumes ("Context Parallelism in vLLM Omni Neuron",
+ * §Self-Attention: o_proj after _nf_attend).  Same arithmetic as
+ * r3d_attn_fwd: the values are identical, only their placement differs.
+ * Errors: as r3d_attn_fwd.
+ */
+R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                              int64_t kv_chunk, int32_t dtype, void* stream);
+
+/*
  * r3d_lse_merge — combine n partial attention results of the same queries
  * against disjoint key sets (the ring-attention combine: each ring step
  * attends one K/V shard, "Context Parallelism in vLLM Omni Neuron",

@@ -6,8 +6,8 @@ torch tensors that already live on the GPU, passes their device pointers,
 sizes and torch's current HIP stream to the library, and maps error codes to
 exceptions.  Every step of the computation runs in the library's HIP
 kernels; there is no fallback.  If the library is missing, importing this
-package raises ImportError (build it with ``python -m
-long_sequence_attention_rope3d_amd.build``).
+package raises ImportError (build it with ``python
+long_sequence_attention_rope3d_amd/build.py``).
 
 Calls (same names as the C entry points without the ``r3d_`` prefix):
   rope3d_apply(x, grid, split, theta=10000.0, out=None)
@@ -48,7 +48,7 @@ class _RopeDesc(ctypes.Structure):
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m long_sequence_attention_rope3d_amd.build` "
+            f"{_LIB_PATH} is not built; run `python long_sequence_attention_rope3d_amd/build.py` "
             "(there is no CPU fallback)")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
@@ -56,8 +56,10 @@ def _load():
     lib.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64,
                                              ctypes.POINTER(_RopeDesc), P]
     lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P]
+    lib.r3d_attn_fwd_bshd.argtypes = lib.r3d_attn_fwd.argtypes
     lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
-    for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd", "r3d_lse_merge"):
+    for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
+              "r3d_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     lib.r3d_last_error.restype = ctypes.c_char_p
     lib.r3d_last_error.argtypes = []
@@ -162,12 +164,15 @@ def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
              kv_chunk: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             return_lse: bool = True):
+             return_lse: bool = True, out_layout: str = "bhsd"):
     """Blockwise non-causal attention. q [B,H,Sq,D], k/v [B,H,Skv,D] ->
-    (out [B,H,Sq,D], lse [B,H,Sq] fp32 natural log) — or out alone if
-    return_lse is False and no lse buffer is given."""
+    (out, lse [B,H,Sq] fp32 natural log) — or out alone if return_lse is False
+    and no lse buffer is given.  out is [B,H,Sq,D] (out_layout="bhsd") or
+    token-major [B,Sq,H,D] (out_layout="bshd", r3d_attn_fwd_bshd)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
+    if out_layout not in ("bhsd", "bshd"):
+        raise ValueError(f"out_layout must be 'bhsd' or 'bshd', got {out_layout!r}")
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
     if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
@@ -176,17 +181,19 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
         raise ValueError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    oshape = (B, H, Sq, D) if out_layout == "bhsd" else (B, Sq, H, D)
     if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+        out = torch.empty(oshape, dtype=q.dtype, device=q.device)
+    if tuple(out.shape) != oshape or out.dtype != q.dtype:
+        raise ValueError(f"out must be {list(oshape)} of q's dtype")
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
-    _check(_lib.r3d_attn_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                             _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
-                             float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd")
+    fn = _lib.r3d_attn_fwd if out_layout == "bhsd" else _lib.r3d_attn_fwd_bshd
+    _check(fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+              _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+              float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd")
     return (out, lse) if lse is not None else out
 
 

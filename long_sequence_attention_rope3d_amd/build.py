@@ -1,6 +1,9 @@
 """Builds librope3d_attn.so in-tree with hipcc for gfx950.
 
-    python -m long_sequence_attention_rope3d_amd.build [-v]
+    python long_sequence_attention_rope3d_amd/build.py [-v]
+
+(run as a file: importing the package first would try to load the library
+this builds).
 
 Each HIP source under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into lib/librope3d_attn.so.  Kernels are launched

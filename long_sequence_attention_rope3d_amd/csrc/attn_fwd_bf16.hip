@@ -250,8 +250,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int D>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t Sq, int64_t Skv, float c, uint32_t qsign,
-    int64_t chunk, int n_qt, int n_blocks) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
+    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
   __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
@@ -464,7 +464,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   // The last tile closed a chunk, so acc = O and m = L (log2).
   // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
   if (qrow < Sq) {
-    uint16_t* op = out + (bh * Sq + qrow) * D;
+    // out row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major).
+    const int64_t b = bh / H;
+    const int64_t orow = out_bshd ? (b * Sq + qrow) * H + (bh - b * H) : bh * Sq + qrow;
+    uint16_t* op = out + orow * D;
 #pragma unroll
     for (int b = 0; b < G::kDBlk; ++b)
 #pragma unroll
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
                             int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                            hipStream_t stream) {
+                            bool out_bshd, hipStream_t stream) {
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
   const int n_blocks = (int)(B * H * n_qt);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
@@ -491,11 +494,11 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const auto* vp = static_cast<const uint16_t*>(v);
   auto* op = static_cast<uint16_t*>(out);
   if (D == 64)
-    attn_bf16_kernel<64><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, Sq, Skv, c, qsign, kv_chunk, n_qt,
-                                                             n_blocks);
+    attn_bf16_kernel<64><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk,
+                                                             n_qt, n_blocks, out_bshd ? 1 : 0);
   else
-    attn_bf16_kernel<128><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, Sq, Skv, c, qsign, kv_chunk,
-                                                              n_qt, n_blocks);
+    attn_bf16_kernel<128><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk,
+                                                              n_qt, n_blocks, out_bshd ? 1 : 0);
   return hipGetLastError();
 }
 

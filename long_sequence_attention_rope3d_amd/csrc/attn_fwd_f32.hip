@@ -24,8 +24,9 @@ constexpr int kBN = 16;
 template <int D>
 __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                          const float* __restrict__ v, float* __restrict__ out,
-                                                         float* __restrict__ lse, int64_t Sq, int64_t Skv,
-                                                         float scale, int64_t chunk, int64_t n_qt) {
+                                                         float* __restrict__ lse, int64_t H, int64_t Sq,
+                                                         int64_t Skv, float scale, int64_t chunk, int64_t n_qt,
+                                                         int out_bshd) {
   __shared__ float ks[kBN][D];
   __shared__ float vs[kBN][D];
   __shared__ float orun[kRows][D + 1];
@@ -93,8 +94,11 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
     L = Ln;
   }
   if (valid) {
+    // out row of (b, h, qi): [B, H, Sq, D], or [B, Sq, H, D] (token-major).
+    const int64_t b = bh / H;
+    const int64_t orow = out_bshd ? (b * Sq + qi) * H + (bh - b * H) : bh * Sq + qi;
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[(bh * Sq + qi) * D + d] = orun[t][d];
+    for (int d = 0; d < D; ++d) out[orow * D + d] = orun[t][d];
     if (lse) lse[bh * Sq + qi] = L;
   }
 }
@@ -103,13 +107,15 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
 
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t B,
                            int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                           hipStream_t stream) {
+                           bool out_bshd, hipStream_t stream) {
   const int64_t n_qt = (Sq + kRows - 1) / kRows;
   const unsigned grid = (unsigned)(n_qt * B * H);
   if (D == 64)
-    attn_f32_kernel<64><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, Sq, Skv, scale, kv_chunk, n_qt);
+    attn_f32_kernel<64><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
+                                                    out_bshd ? 1 : 0);
   else
-    attn_f32_kernel<128><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, Sq, Skv, scale, kv_chunk, n_qt);
+    attn_f32_kernel<128><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
+                                                     out_bshd ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -186,9 +186,12 @@ R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg
                     "joint_concat_permute");
 }
 
-R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                         int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                         int64_t kv_chunk, int32_t dtype, void* stream) {
+namespace {
+// Shared by both output layouts: the validation is identical (out has the
+// same number of elements either way).
+int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                  int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk, int32_t dtype,
+                  bool out_bshd, void* stream) {
   const int es = elt_size(dtype);
   if (!es) return fail(R3D_EUNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
   if (!q || !k || !v || !out) return fail(R3D_EINVAL, "attn_fwd: NULL tensor pointer");
@@ -215,11 +218,24 @@ R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   hipError_t e;
   if (dtype == R3D_BF16)
-    e = r3d::launch_attn_bf16(q, k, v, out, lse, B, H, Sq, Skv, D, scale, chunk, (hipStream_t)stream);
+    e = r3d::launch_attn_bf16(q, k, v, out, lse, B, H, Sq, Skv, D, scale, chunk, out_bshd, (hipStream_t)stream);
   else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
-                             D, scale, chunk, (hipStream_t)stream);
+                             D, scale, chunk, out_bshd, (hipStream_t)stream);
   return hip_status(e, "attn_fwd");
+}
+}  // namespace
+
+R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                         int64_t kv_chunk, int32_t dtype, void* stream) {
+  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, false, stream);
+}
+
+R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                              int64_t kv_chunk, int32_t dtype, void* stream) {
+  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, true, stream);
 }
 
 R3D_API int r3d_lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,

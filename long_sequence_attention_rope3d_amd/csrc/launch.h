@@ -37,15 +37,16 @@ hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t N
 hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H,
                           int64_t D, const RopeArgs& rope, hipStream_t stream);
 
-// attn_fwd, bf16 MFMA path (D = 64 or 128).
+// attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
+// instead of [B, H, Sq, D].
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                            int64_t kv_chunk, hipStream_t stream);
+                            int64_t kv_chunk, bool out_bshd, hipStream_t stream);
 
-// attn_fwd, fp32 path (D = 64 or 128).
+// attn_fwd, fp32 path (D = 64 or 128); out_bshd as above.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                           int64_t kv_chunk, hipStream_t stream);
+                           int64_t kv_chunk, bool out_bshd, hipStream_t stream);
 
 // lse_merge: parts [n, rows, D] + lse [n, rows] -> out [rows, D] (+ lse_out).
 hipError_t launch_lse_merge(const void* parts, const float* lse_parts, int32_t n, bool parts_bf16,

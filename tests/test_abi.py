@@ -29,7 +29,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd",
-                                  "r3d_lse_merge", "r3d_last_error", "r3d_version"])
+                                  "r3d_attn_fwd_bshd", "r3d_lse_merge", "r3d_last_error", "r3d_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -55,6 +55,7 @@ P = ctypes.c_void_p
 I32, I64 = ctypes.c_int32, ctypes.c_int64
 F = ctypes.c_float
 LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P]
+LIB.r3d_attn_fwd_bshd.argtypes = LIB.r3d_attn_fwd.argtypes
 LIB.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64, P, P]
 LIB.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
@@ -63,11 +64,11 @@ LIB.r3d_last_error.restype = ctypes.c_char_p
 A, B_, C, O, L_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 
 
-def _attn(**kw):
+def _attn(fn="r3d_attn_fwd", **kw):
     a = dict(q=A, k=B_, v=C, out=O, lse=L_, B=1, H=2, Sq=64, Skv=64, D=128, scale=0.125,
              kv_chunk=0, dtype=1)
     a.update(kw)
-    return LIB.r3d_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Sq"],
+    return getattr(LIB, fn)(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Sq"],
                             a["Skv"], a["D"], a["scale"], a["kv_chunk"], a["dtype"], None)
 
 
@@ -85,8 +86,9 @@ def _attn(**kw):
     (dict(lse=O + 1024), -1, "overlaps"),
     (dict(B=1 << 40, H=1 << 20), -1, "too large"),
 ])
-def test_attn_fwd_rejects(kw, status, needle):
-    assert _attn(**kw) == status
+@pytest.mark.parametrize("fn", ["r3d_attn_fwd", "r3d_attn_fwd_bshd"])
+def test_attn_fwd_rejects(fn, kw, status, needle):
+    assert _attn(fn, **kw) == status
     assert needle in LIB.r3d_last_error().decode()
 
 
@@ -153,3 +155,5 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         r3d.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="out_layout"):
+        r3d.attn_fwd(q, q, q, out_layout="sbhd")

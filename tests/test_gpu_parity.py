@@ -188,6 +188,42 @@ def test_attn_fwd_without_lse(gpu):
 
 
 # ------------------------------------------------------------------------------------------
+# Token-major output (r3d_attn_fwd_bshd): the same values, placed [B, Sq, H, D]
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D,B,H,Sq,Skv,kv_chunk", [
+    (torch.bfloat16, 128, 2, 3, 300, 333, 128),
+    (torch.bfloat16, 128, 1, 5, 385, 1000, 0),     # 384-row tile + a 1-row tail
+    (torch.bfloat16, 64, 2, 3, 130, 257, 100),
+    (torch.float32, 64, 2, 3, 100, 257, 50),
+    (torch.float32, 128, 1, 2, 70, 130, 0),
+])
+def test_attn_bshd_is_the_bhsd_result_relaid(gpu, dtype, D, B, H, Sq, Skv, kv_chunk):
+    say(f"bshd {dtype} D={D} B={B} H={H} Sq={Sq} Skv={Skv} chunk={kv_chunk}")
+    q = _rand((B, H, Sq, D), dtype, 81).to(gpu)
+    k = _rand((B, H, Skv, D), dtype, 82).to(gpu)
+    v = _rand((B, H, Skv, D), dtype, 83).to(gpu)
+    a, la = r3d.attn_fwd(q, k, v, kv_chunk=kv_chunk)
+    b, lb = r3d.attn_fwd(q, k, v, kv_chunk=kv_chunk, out_layout="bshd")
+    torch.cuda.synchronize()
+    assert tuple(b.shape) == (B, Sq, H, D)
+    assert torch.equal(b, a.transpose(1, 2).contiguous())    # bit-exact: only placement differs
+    assert torch.equal(la, lb)
+
+
+def test_attn_bshd_matches_oracle(gpu):
+    q = _rand((2, 3, 200, 128), torch.bfloat16, 91)
+    k = _rand((2, 3, 450, 128), torch.bfloat16, 92)
+    v = _rand((2, 3, 450, 128), torch.bfloat16, 93)
+    scale = 1.0 / math.sqrt(128)
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=128,
+                            out_layout="bshd")
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
+    check_attn(out.transpose(1, 2), lse, ref_out, ref_lse, torch.bfloat16, "bshd vs oracle")
+
+
+# ------------------------------------------------------------------------------------------
 # GPU invariants
 # ------------------------------------------------------------------------------------------
 
