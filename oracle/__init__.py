@@ -64,6 +64,8 @@ def _load():
     lib.oracle_rope_vec.argtypes = [P, P, I64, I64, I64, I64, I, I, I, D]
     lib.oracle_rope3d.argtypes = [P, P, I64, I64, I64, I64, I64, I64, I64, I, I, I, D]
     lib.oracle_rope3d.restype = I
+    lib.oracle_rms_norm.argtypes = [P, P, I64, I64, P, D]
+    lib.oracle_rms_norm.restype = I
     lib.oracle_joint_concat_permute.argtypes = [P, P, I, P, I64, I64, I64, I64]
     lib.oracle_joint_concat_permute.restype = I
     lib.oracle_attention.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, D]
@@ -136,6 +138,22 @@ def rope3d(x, grid, split, theta: float) -> np.ndarray:
                                float(theta))
     if rc != 0:
         raise ValueError("oracle_rope3d: grid/split do not match the tensor")
+    return y
+
+
+# --- QK-norm --------------------------------------------------------------------
+
+def rms_norm(x, w, eps: float) -> np.ndarray:
+    """x: [..., n] -> x / sqrt(mean(x^2 over the last axis) + eps) * w[n] (fp64)."""
+    x = _f64(x)
+    w = _f64(w).reshape(-1)
+    n = x.shape[-1]
+    if w.size != n:
+        raise ValueError("rms_norm: weight length must equal the last axis")
+    y = np.empty_like(x)
+    rc = _load().oracle_rms_norm(_ptr(x), _ptr(y), x.size // n, n, _ptr(w), float(eps))
+    if rc != 0:
+        raise ValueError("oracle_rms_norm: n <= 0 or eps < 0")
     return y
 
 
@@ -223,17 +241,32 @@ def lse_merge(parts, lse_parts):
 
 # --- the whole path -------------------------------------------------------------
 
-def prepare_qkv(q_segs, k_segs, v_segs, grid, split, theta, io_dtype):
-    """Steps 1-3 of the pipeline: fp64 RoPE on segment 0 of Q and K, rounding of
-    the rotated values to ``io_dtype`` ("bf16" or "f32"), then the joint
-    concat + [B,S,H,D] -> [B,H,S,D] re-layout.  Inputs are fp64 arrays holding
-    the exact values of the stored inputs, one [B,S_i,H,D] array per segment,
-    video first.  Returns fp64 q, k, v in [B,H,S,D]."""
-    def rotated(segs):
-        r0 = round_to(rope3d(segs[0], grid, split, theta), io_dtype)
-        return [r0] + [_f64(s) for s in segs[1:]]
-    q = joint_concat_permute(rotated(q_segs))
-    k = joint_concat_permute(rotated(k_segs))
+def prepare_qkv(q_segs, k_segs, v_segs, grid, split, theta, io_dtype, norm_q=None, norm_k=None,
+                eps: float = 1e-6):
+    """Steps 1-3 of the pipeline: optional RMS QK-norm (norm_q / norm_k: None,
+    or one entry per segment, None or the segment's [H*D] weight vector; the
+    statistic is over each token's H*D values), fp64 RoPE on segment 0 of Q
+    and K, one rounding of every changed value to ``io_dtype`` ("bf16" or
+    "f32"), then the joint concat + [B,S,H,D] -> [B,H,S,D] re-layout.  Inputs
+    are fp64 arrays holding the exact values of the stored inputs, one
+    [B,S_i,H,D] array per segment, video first.  Returns fp64 q, k, v in
+    [B,H,S,D]."""
+    def prepared(segs, norms):
+        out = []
+        for i, s in enumerate(segs):
+            x = _f64(s)
+            changed = False
+            if norms is not None and norms[i] is not None:
+                B, S, H, D = x.shape
+                x = rms_norm(x.reshape(B, S, H * D), norms[i], eps).reshape(B, S, H, D)
+                changed = True
+            if i == 0:
+                x = rope3d(x, grid, split, theta)
+                changed = True
+            out.append(round_to(x, io_dtype) if changed else x)
+        return out
+    q = joint_concat_permute(prepared(q_segs, norm_q))
+    k = joint_concat_permute(prepared(k_segs, norm_k))
     v = joint_concat_permute([_f64(s) for s in v_segs])
     return q, k, v
 

@@ -3,7 +3,8 @@
  *
  * A plain, slow, obviously correct fp64 CPU implementation of what the
  * library computes: 3-D rotary position embedding on the video tokens of Q/K,
- * the joint concat + sequence->head re-layout, full non-causal softmax
+ * the RMS QK-norm that precedes it, the joint concat + sequence->head
+ * re-layout, full non-causal softmax
  * attention, a separately written chunked form with a log-sum-exp merge, and
  * the n-way log-sum-exp merge of partial attention outputs.
  *
@@ -144,6 +145,38 @@ int oracle_rope3d(const double* x, double* y, int64_t B, int64_t Nv, int64_t H, 
       const int64_t o = (r * H + hd) * D;
       oracle_rope_vec(x + o, y + o, D, t, h, w, d_t, d_h, d_w, theta);
     }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* QK-norm: RMS normalisation of a token's whole hidden vector.              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * x, y: [rows, n], n = H*D: a token's projected q (or k) before it is split
+ * into heads; w: [n].
+ *     y[r, i] = x[r, i] / sqrt(mean_j x[r, j]^2 + eps) * w[i].
+ * "Context Parallelism in vLLM Omni Neuron", §Self-Attention with Context
+ * Parallelism: norm_q / norm_k act on the projected q, k of shape [B, S, H]
+ * (hidden size H = heads x head_dim) before .unflatten(2, (num_heads,
+ * head_dim)) and before the rotary embedding; §Distributed Normalization:
+ * the norm's statistic is a sum of squares over the hidden dimension.
+ * Reading (the pages print neither the formula nor eps): root-mean-square
+ * normalisation with a learned per-channel weight, the mean square taken
+ * over the whole hidden vector, eps added to the mean square.
+ * Returns -1 if n <= 0 or eps < 0.
+ */
+int oracle_rms_norm(const double* x, double* y, int64_t rows, int64_t n, const double* w,
+                    double eps) {
+  if (n <= 0 || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* xr = x + r * n;
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += xr[i] * xr[i];
+    const double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; ++i) y[r * n + i] = xr[i] * inv * w[i];
   }
   return 0;
 }

@@ -348,3 +348,75 @@ def test_pipeline_against_torch_route():
     want = torch.softmax(logits, -1) @ tv
     np.testing.assert_allclose(out, want.numpy(), atol=1e-6)
     np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).numpy(), atol=1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# QK-norm (RMS over a token's whole hidden vector, "Context Parallelism in vLLM Omni Neuron",
+# §Self-Attention with Context Parallelism: norm_q / norm_k before unflatten and RoPE)
+# ---------------------------------------------------------------------------------------------
+
+def test_rms_norm_worked_example():
+    # mean of squares of (1, 2, 3, 4) is 30/4 = 7.5
+    y = oracle.rms_norm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.ones(4), 0.0)
+    np.testing.assert_allclose(y, np.array([[1.0, 2.0, 3.0, 4.0]]) / math.sqrt(7.5), rtol=1e-15)
+
+
+def test_rms_norm_constant_row_and_eps():
+    # a row of a's: mean square a^2, so y = a / sqrt(a^2 + eps) * w exactly in the formula
+    a, eps = -3.0, 0.5
+    w = RNG.standard_normal(6)
+    y = oracle.rms_norm(np.full((1, 6), a), w, eps)
+    np.testing.assert_allclose(y[0], a / math.sqrt(a * a + eps) * w, rtol=1e-15)
+
+
+def test_rms_norm_output_has_unit_rms_and_is_scale_free():
+    x = RNG.standard_normal((5, 384)) * RNG.uniform(0.1, 10.0, (5, 1))
+    y = oracle.rms_norm(x, np.ones(384), 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(axis=1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rms_norm(-7.5 * x, np.ones(384), 0.0), -y, rtol=1e-14)
+
+
+def test_rms_norm_weight_is_per_channel():
+    x = RNG.standard_normal((3, 64))
+    w = np.zeros(64)
+    w[17] = 2.5
+    y = oracle.rms_norm(x, w, 1e-6)
+    assert (y[:, :17] == 0).all() and (y[:, 18:] == 0).all()
+    np.testing.assert_allclose(y[:, 17], 2.5 * x[:, 17] / np.sqrt((x * x).mean(1) + 1e-6), rtol=1e-14)
+
+
+def test_rms_norm_matches_torch():
+    x = RNG.standard_normal((7, 3 * 128))
+    w = RNG.standard_normal(3 * 128)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(x), (3 * 128,), weight=torch.from_numpy(w),
+                                        eps=1e-6)
+    np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-6), want.numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_qknorm_then_rope_keeps_unit_rms_per_token():
+    # RoPE rotates pairs, so after an RMS norm with w = 1, eps = 0 every token's hidden
+    # vector (all heads) still has RMS 1; the other segments are normalised and not rotated.
+    grid, sp = (2, 3, 4), (16, 24, 24)
+    B, H, D = 2, 3, 64
+    segs = [RNG.standard_normal((B, 24, H, D)) * 3.0, RNG.standard_normal((B, 5, H, D))]
+    v = [np.zeros_like(s) for s in segs]
+    ones = np.ones(H * D)
+    q, _, _ = oracle.prepare_qkv(segs, segs, v, grid, sp, THETA, "f32", norm_q=[ones, ones],
+                                 norm_k=None, eps=0.0)
+    rms = np.sqrt((q.transpose(0, 2, 1, 3) ** 2).reshape(B, 29, H * D).mean(-1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-6)       # f32 storage rounding only
+    _, k, _ = oracle.prepare_qkv(segs, segs, v, grid, sp, THETA, "f32", norm_q=[ones, ones])
+    # no norm on K: segment 1 is copied exactly
+    np.testing.assert_array_equal(k[:, :, 24:], segs[1].transpose(0, 2, 1, 3))
+
+
+def test_qknorm_segment_without_weights_is_untouched():
+    grid, sp = (1, 2, 2), (0, 32, 32)
+    B, H, D = 1, 2, 64
+    segs = [RNG.standard_normal((B, 4, H, D)), RNG.standard_normal((B, 3, H, D))]
+    v = [np.zeros_like(s) for s in segs]
+    w = RNG.standard_normal(H * D)
+    q1, _, _ = oracle.prepare_qkv(segs, segs, v, grid, sp, THETA, "f32", norm_q=[w, None])
+    q0, _, _ = oracle.prepare_qkv(segs, segs, v, grid, sp, THETA, "f32")
+    np.testing.assert_array_equal(q1[:, :, 4:], q0[:, :, 4:])
+    assert not np.array_equal(q1[:, :, :4], q0[:, :, :4])
