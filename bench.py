@@ -212,6 +212,14 @@ def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps
     ms = timed(lambda: r3d.joint_concat_permute(segs["v"], None, out=q))
     res["joint_concat_permute"] = {"ms": round(ms, 4), "bytes": 2 * n_all * es,
                                    "GBps": round(2 * n_all * es / ms / 1e6, 1)}
+    # QK-norm fused ahead of RoPE and the re-layout (weights for every segment)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 11)
+    wts = [1.0 + 0.1 * torch.randn(w.H * w.D, device=dev, generator=g) for _ in segs["q"]]
+    ms = timed(lambda: r3d.joint_concat_permute(segs["q"], rope, out=q, norm=wts))
+    res["joint_concat_permute_qknorm_rope"] = {"ms": round(ms, 4), "bytes": 2 * n_all * es,
+                                               "GBps": round(2 * n_all * es / ms / 1e6, 1)}
+    del wts
     x = segs["q"][0]
     y = torch.empty_like(x)
     ms = timed(lambda: r3d.rope3d_apply(x, w.grid, w.split, w.theta, out=y))

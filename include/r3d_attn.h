@@ -104,6 +104,31 @@ R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg
                                      void* stream);
 
 /*
+ * r3d_joint_concat_permute_qknorm — r3d_joint_concat_permute with the QK-norm
+ * fused in front of the rotation ("Context Parallelism in vLLM Omni Neuron",
+ * §Self-Attention with Context Parallelism: norm_q / norm_k act on the
+ * projected q, k — one token's H*D values before .unflatten into heads — and
+ * then the rotary embedding is applied; §Distributed Normalization: the
+ * statistic is the sum of squares over that hidden dimension):
+ *     x <- x / sqrt(mean(x^2 over the token's H*D values) + eps) * w
+ * for every token of segment i when norm_w[i] != NULL, then RoPE on segment 0
+ * when rope_seg0 != NULL, then the re-layout.  Norm, rotation and rounding
+ * are fp64 with one round-to-nearest-even store (the composition is rounded
+ * once, not after each step).
+ *   norm_w : HOST array of n_segs pointers, each NULL (segment copied, or only
+ *            rotated) or a DEVICE fp32 vector of H*D weights, 16-byte aligned.
+ *   eps    : finite, >= 0 (the pages give no value; 1e-6 is a common choice).
+ *   D      : 64 or 128 when any weight vector is given.
+ *   Other arguments as r3d_joint_concat_permute.
+ * Errors: as r3d_joint_concat_permute, plus R3D_EINVAL for a NULL norm_w
+ * array, misaligned weights, bad eps or out overlapping weights.
+ */
+R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64_t* seg_len,
+                                            int32_t n_segs, const float* const* norm_w, double eps,
+                                            void* out, int32_t dtype, int64_t B, int64_t H, int64_t D,
+                                            const r3d_rope_desc* rope_seg0, void* stream);
+
+/*
  * r3d_attn_fwd — full non-causal multi-head attention, blockwise.
  * ("Context Parallelism in vLLM Omni Neuron", §Self-Attention:
  * _nf_attend(query, key, value, scale) on [B, N, S, D]; §Ring attention and

@@ -55,11 +55,13 @@ def _load():
     lib.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, ctypes.POINTER(_RopeDesc), P]
     lib.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64,
                                              ctypes.POINTER(_RopeDesc), P]
+    lib.r3d_joint_concat_permute_qknorm.argtypes = [P, P, I32, P, ctypes.c_double, P, I32, I64, I64, I64,
+                                                    ctypes.POINTER(_RopeDesc), P]
     lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P]
     lib.r3d_attn_fwd_bshd.argtypes = lib.r3d_attn_fwd.argtypes
     lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
-    for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
-              "r3d_lse_merge"):
+    for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_joint_concat_permute_qknorm",
+              "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     lib.r3d_last_error.restype = ctypes.c_char_p
     lib.r3d_last_error.argtypes = []
@@ -132,9 +134,14 @@ def rope3d_apply(x: torch.Tensor, grid, split, theta: float = 10000.0,
 
 
 def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = None,
-                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         out: Optional[torch.Tensor] = None,
+                         norm: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                         eps: float = 1e-6) -> torch.Tensor:
     """segs: [B, S_i, H, D] tensors (video first) -> [B, H, sum S_i, D].
-    With ``rope``, segment 0 is rotated while it is copied."""
+    With ``rope``, segment 0 is rotated while it is copied.  With ``norm`` (one
+    entry per segment: None or a float32 [H*D] weight vector on the device),
+    each token of a weighted segment is first RMS-normalised over its H*D
+    values (QK-norm, r3d_joint_concat_permute_qknorm)."""
     segs = list(segs)
     if not segs:
         raise ValueError("need at least one segment")
@@ -154,11 +161,26 @@ def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = 
         *[(_dev(s, "segment") if s.shape[1] > 0 else None) for s in segs])
     lens = (ctypes.c_int64 * len(segs))(*[int(s.shape[1]) for s in segs])
     desc = rope.desc() if rope is not None else None
-    _check(_lib.r3d_joint_concat_permute(ctypes.cast(ptrs, ctypes.c_void_p),
-                                         ctypes.cast(lens, ctypes.c_void_p), len(segs),
-                                         _dev(out, "out"), _dtype_code(out), B, H, D,
-                                         ctypes.byref(desc) if desc is not None else None,
-                                         _stream(out)), "joint_concat_permute")
+    rope_arg = ctypes.byref(desc) if desc is not None else None
+    if norm is None:
+        _check(_lib.r3d_joint_concat_permute(ctypes.cast(ptrs, ctypes.c_void_p),
+                                             ctypes.cast(lens, ctypes.c_void_p), len(segs),
+                                             _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
+                                             _stream(out)), "joint_concat_permute")
+        return out
+    norm = list(norm)
+    if len(norm) != len(segs):
+        raise ValueError("norm needs one entry (None or a weight vector) per segment")
+    for w in norm:
+        if w is not None and (w.dtype != torch.float32 or w.numel() != H * D or not w.is_contiguous()):
+            raise ValueError("norm weights must be contiguous float32 vectors of H*D values")
+    wptrs = (ctypes.c_void_p * len(segs))(*[(_dev(w, "norm weight") if w is not None else None)
+                                             for w in norm])
+    _check(_lib.r3d_joint_concat_permute_qknorm(ctypes.cast(ptrs, ctypes.c_void_p),
+                                                ctypes.cast(lens, ctypes.c_void_p), len(segs),
+                                                ctypes.cast(wptrs, ctypes.c_void_p), float(eps),
+                                                _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
+                                                _stream(out)), "joint_concat_permute_qknorm")
     return out
 
 

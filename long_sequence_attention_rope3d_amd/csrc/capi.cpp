@@ -136,10 +136,11 @@ R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, i
                     "rope3d_apply");
 }
 
-R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg_len,
-                                     int32_t n_segs, void* out, int32_t dtype, int64_t B,
-                                     int64_t H, int64_t D, const r3d_rope_desc* rope_seg0,
-                                     void* stream) {
+namespace {
+// Shared by the plain and the QK-norm entry points (norm_w == NULL: no norm).
+int permute_impl(const void* const* segs, const int64_t* seg_len, int32_t n_segs, const float* const* norm_w,
+                 double eps, void* out, int32_t dtype, int64_t B, int64_t H, int64_t D,
+                 const r3d_rope_desc* rope_seg0, void* stream) {
   const int es = elt_size(dtype);
   if (!es) return fail(R3D_EUNSUPPORTED, "joint_concat_permute: unknown dtype %d", dtype);
   if (!segs || !seg_len) return fail(R3D_EINVAL, "joint_concat_permute: NULL segment arrays");
@@ -182,8 +183,42 @@ R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg
     int st = build_rope(rope_seg0, D, seg_len[0], ra);
     if (st != R3D_OK) return st;
   }
+  if (norm_w) {
+    if (!std::isfinite(eps) || eps < 0.0)
+      return fail(R3D_EINVAL, "joint_concat_permute: norm eps must be finite and >= 0");
+    int64_t nw;
+    if (!product(nw, {H, D}) || nw > kMaxElems) return fail(R3D_EINVAL, "joint_concat_permute: H*D too large");
+    for (int i = 0; i < n_segs; ++i) {
+      if (!norm_w[i]) continue;
+      if (D != 64 && D != 128)
+        return fail(R3D_EUNSUPPORTED, "joint_concat_permute: QK-norm needs D in {64, 128}, got %lld", (long long)D);
+      if (!aligned16(norm_w[i]))
+        return fail(R3D_EINVAL, "joint_concat_permute: norm weights %d not 16-byte aligned", i);
+      if (overlap(norm_w[i], nw * 4, out, n_out * es))
+        return fail(R3D_EINVAL, "joint_concat_permute: out overlaps the norm weights of segment %d", i);
+      if (seg_len[i] > 0) sa.norm = 1;
+      sa.norm_w[i] = norm_w[i];
+    }
+    sa.norm_eps = eps;
+  }
   return hip_status(r3d::launch_permute(sa, out, dtype == R3D_BF16, B, H, D, ra, (hipStream_t)stream),
                     "joint_concat_permute");
+}
+}  // namespace
+
+R3D_API int r3d_joint_concat_permute(const void* const* segs, const int64_t* seg_len,
+                                     int32_t n_segs, void* out, int32_t dtype, int64_t B,
+                                     int64_t H, int64_t D, const r3d_rope_desc* rope_seg0,
+                                     void* stream) {
+  return permute_impl(segs, seg_len, n_segs, nullptr, 0.0, out, dtype, B, H, D, rope_seg0, stream);
+}
+
+R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64_t* seg_len,
+                                            int32_t n_segs, const float* const* norm_w, double eps,
+                                            void* out, int32_t dtype, int64_t B, int64_t H, int64_t D,
+                                            const r3d_rope_desc* rope_seg0, void* stream) {
+  if (!norm_w) return fail(R3D_EINVAL, "joint_concat_permute: NULL norm weight array");
+  return permute_impl(segs, seg_len, n_segs, norm_w, eps, out, dtype, B, H, D, rope_seg0, stream);
 }
 
 namespace {

@@ -26,6 +26,11 @@ struct SegArgs {
   int64_t off[kMaxSegs];
   int32_t n;
   int64_t S;  // sum of len
+  // QK-norm: per segment NULL (no norm) or an fp32 weight vector [H*D]; the
+  // RMS statistic is over each token's H*D values.
+  const float* norm_w[kMaxSegs];
+  double norm_eps;
+  int32_t norm;  // any norm_w non-NULL
 };
 
 // rope3d_apply: [B, Nv, H, D] -> [B, Nv, H, D] (may be in place).
@@ -33,7 +38,7 @@ hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t N
                          int64_t D, const RopeArgs& rope, hipStream_t stream);
 
 // joint_concat_permute: segments [B, S_i, H, D] -> [B, H, S, D]; rope.enabled
-// rotates segment 0.
+// rotates segment 0; segs.norm applies the per-segment RMS QK-norm first.
 hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H,
                           int64_t D, const RopeArgs& rope, hipStream_t stream);
 

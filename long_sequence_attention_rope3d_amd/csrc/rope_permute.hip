@@ -9,7 +9,12 @@
 // re-layout):
 //   rope3d_apply         : [B, Nv, H, D] -> [B, Nv, H, D], video tokens rotated
 //   joint_concat_permute : segments [B, S_i, H, D] -> [B, H, S, D], optionally
-//                          rotating segment 0 (video) on the way through.
+//                          rotating segment 0 (video) on the way through, and
+//                          optionally RMS-normalising each token's H*D values
+//                          first (QK-norm: norm_q / norm_k act on the projected
+//                          q, k before they are split into heads and before
+//                          RoPE, same page, §Self-Attention with Context
+//                          Parallelism).
 //
 // Layout of the work.  A block owns kTok consecutive tokens of one batch row
 // and all H heads of them.  Per token, the cos/sin of its D/2 pair angles are
@@ -82,13 +87,75 @@ __device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const double2* cs, int ch
   return v;
 }
 
+// QK-norm of one 16-byte chunk, then (cs != nullptr) its rotation: every
+// element x becomes x * r * w (r = 1/sqrt(mean square + eps) of its token,
+// w its channel's weight, `w` pointing at the chunk's first channel), the
+// pairs are rotated, all in fp64, and each value is rounded once.
+template <bool BF16>
+__device__ __forceinline__ u32x4 norm_rotate_chunk(u32x4 v, double r, const float* w, const double2* cs,
+                                                   int chunk) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double x0 = (double)__uint_as_float(v[q] << 16) * r * (double)w[2 * q];
+      double x1 = (double)__uint_as_float(v[q] & 0xffff0000u) * r * (double)w[2 * q + 1];
+      if (cs) {
+        const double2 c = cs[chunk * 4 + q];
+        const double y0 = x0 * c.x - x1 * c.y, y1 = x0 * c.y + x1 * c.x;
+        x0 = y0;
+        x1 = y1;
+      }
+      v[q] = f64_to_bf16(x0) | (f64_to_bf16(x1) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      double x0 = (double)__uint_as_float(v[2 * p]) * r * (double)w[2 * p];
+      double x1 = (double)__uint_as_float(v[2 * p + 1]) * r * (double)w[2 * p + 1];
+      if (cs) {
+        const double2 c = cs[chunk * 2 + p];
+        const double y0 = x0 * c.x - x1 * c.y, y1 = x0 * c.y + x1 * c.x;
+        x0 = y0;
+        x1 = y1;
+      }
+      v[2 * p] = __float_as_uint((float)x0);
+      v[2 * p + 1] = __float_as_uint((float)x1);
+    }
+  }
+  return v;
+}
+
+// Sum of squares of the values in one 16-byte chunk (exact products in fp64).
+template <bool BF16>
+__device__ __forceinline__ double chunk_sumsq(u32x4 v) {
+  double s = 0.0;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double x0 = (double)__uint_as_float(v[q] << 16), x1 = (double)__uint_as_float(v[q] & 0xffff0000u);
+      s += x0 * x0 + x1 * x1;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double x = (double)__uint_as_float(v[q]);
+      s += x * x;
+    }
+  }
+  return s;
+}
+
 // PERMUTE = false: rope3d_apply layout (src and dst both [B, S, H, D], one
 //                  segment, every token rotated).
 // PERMUTE = true : joint concat into [B, H, S, D]; ROPE rotates segment 0.
-template <bool BF16, bool PERMUTE, bool ROPE>
+// NORM (with PERMUTE, D in {64, 128}): segments with a weight vector get the
+// RMS QK-norm before the rotation.
+template <bool BF16, bool PERMUTE, bool ROPE, bool NORM>
 __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, void* out,
                                                                 int H, int D, int64_t n_tb, RopeArgs rope) {
   __shared__ double2 cs[kTok][kMaxPairs];
+  __shared__ double red[NORM ? kThreads : 1];
+  __shared__ double rnorm[kTok];
   const int64_t b = (int64_t)blockIdx.x / n_tb;
   const int64_t tok0 = ((int64_t)blockIdx.x - b * n_tb) * kTok;
   const int64_t S = segs.S;
@@ -116,25 +183,59 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
   }
 
   const int per_h = kTok * cpr;
-  if (per_h <= kThreads && kThreads % per_h == 0) {
+  // (The host allows NORM only for D in {64, 128}, which always takes this branch.)
+  if (NORM || (per_h <= kThreads && kThreads % per_h == 0)) {
     // Each thread keeps one (token, chunk) slot and walks the heads.
     const int slot = threadIdx.x % per_h;
     const int tl = slot / cpr, chunk = slot - tl * cpr;
     const int hstep = kThreads / per_h;
     const int64_t s = tok0 + tl;
-    if (s >= S) return;
+    const bool valid = s < S;
+    if (!NORM && !valid) return;  // with NORM every thread reaches the barriers below
     int seg = 0;
     if constexpr (PERMUTE) {
-      while (seg + 1 < segs.n && s >= segs.off[seg + 1]) ++seg;
+      while (valid && seg + 1 < segs.n && s >= segs.off[seg + 1]) ++seg;
     }
     const int64_t ls = s - segs.off[seg];
     const u32x4* src = reinterpret_cast<const u32x4*>(segs.src[seg]) + ((b * segs.len[seg] + ls) * H) * cpr + chunk;
     u32x4* dst = reinterpret_cast<u32x4*>(out);
     const bool rot = ROPE && seg == 0;
+    const int epc = 16 / (BF16 ? 2 : 4);  // elements per 16-byte chunk
+    const float* wn = nullptr;
+    double r = 1.0;
+    if constexpr (NORM) {
+      // Pass 1: the token's sum of squares over all H*D values.  The threads
+      // of token tl are slots tl*cpr + [0, cpr) of each of the hstep head
+      // groups; their partial sums meet in LDS.
+      wn = valid ? segs.norm_w[seg] : nullptr;
+      double ss = 0.0;
+      if (wn) {
+        for (int h = threadIdx.x / per_h; h < H; h += hstep) ss += chunk_sumsq<BF16>(src[(int64_t)h * cpr]);
+      }
+      red[threadIdx.x] = ss;
+      __syncthreads();
+      if (threadIdx.x < kTok) {
+        double t = 0.0;
+        for (int g = 0; g < hstep; ++g)
+          for (int c = 0; c < cpr; ++c) t += red[g * per_h + threadIdx.x * cpr + c];
+        rnorm[threadIdx.x] = 1.0 / sqrt(t / (double)((int64_t)H * D) + segs.norm_eps);
+      }
+      __syncthreads();
+      if (!valid) return;
+      r = rnorm[tl];
+    }
+    // Pass 2 (the only pass without NORM): normalise / rotate / copy.  With a
+    // norm the rows are read a second time, from the L2 the first pass filled.
 #pragma unroll 4
     for (int h = threadIdx.x / per_h; h < H; h += hstep) {
-      u32x4 v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
-      if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+      u32x4 v;
+      if (NORM && wn) {
+        v = src[(int64_t)h * cpr];
+        v = norm_rotate_chunk<BF16>(v, r, wn + (int64_t)h * D + chunk * epc, rot ? cs[tl] : nullptr, chunk);
+      } else {
+        v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
+        if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+      }
       const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
       __builtin_nontemporal_store(v, dst + o);
     }
@@ -160,15 +261,17 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
   }
 }
 
-template <bool PERMUTE, bool ROPE>
+template <bool PERMUTE, bool ROPE, bool NORM = false>
 hipError_t launch_typed(bool bf16, const SegArgs& segs, void* out, int64_t B, int64_t H, int64_t D,
                         const RopeArgs& rope, hipStream_t stream) {
   const int64_t n_tb = (segs.S + kTok - 1) / kTok;  // token blocks per batch row
   const unsigned grid = (unsigned)(n_tb * B);
   if (bf16)
-    rope_permute_kernel<true, PERMUTE, ROPE><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
+    rope_permute_kernel<true, PERMUTE, ROPE, NORM><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb,
+                                                                                  rope);
   else
-    rope_permute_kernel<false, PERMUTE, ROPE><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
+    rope_permute_kernel<false, PERMUTE, ROPE, NORM><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb,
+                                                                                   rope);
   return hipGetLastError();
 }
 
@@ -187,6 +290,10 @@ hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t N
 
 hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H, int64_t D,
                           const RopeArgs& rope, hipStream_t stream) {
+  if (segs.norm) {
+    if (rope.enabled) return launch_typed<true, true, true>(bf16, segs, out, B, H, D, rope, stream);
+    return launch_typed<true, false, true>(bf16, segs, out, B, H, D, rope, stream);
+  }
   if (rope.enabled) return launch_typed<true, true>(bf16, segs, out, B, H, D, rope, stream);
   return launch_typed<true, false>(bf16, segs, out, B, H, D, rope, stream);
 }

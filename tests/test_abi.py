@@ -28,8 +28,9 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_attn_fwd",
-                                  "r3d_attn_fwd_bshd", "r3d_lse_merge", "r3d_last_error", "r3d_version"])
+    assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute",
+                                  "r3d_joint_concat_permute_qknorm", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
+                                  "r3d_lse_merge", "r3d_last_error", "r3d_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -58,6 +59,7 @@ LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32
 LIB.r3d_attn_fwd_bshd.argtypes = LIB.r3d_attn_fwd.argtypes
 LIB.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64, P, P]
+LIB.r3d_joint_concat_permute_qknorm.argtypes = [P, P, I32, P, ctypes.c_double, P, I32, I64, I64, I64, P, P]
 LIB.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
 LIB.r3d_last_error.restype = ctypes.c_char_p
 
@@ -134,6 +136,28 @@ def test_permute_rejects():
     assert _perm([A] * 9, [1] * 9) == -1         # too many segments
     assert _perm([A], [240], D=64, rope=Rope(2, 8, 14, 16, 24, 24, 1e4)) == -1
     assert _perm([A], [240], D=48, dtype=1, rope=Rope(2, 8, 15, 16, 16, 16, 1e4)) == -2
+
+
+def _permn(ptrs, lens, wts, eps=1e-6, out=O, D=128, dtype=1, rope=None, null_w=False):
+    arr = (P * len(ptrs))(*ptrs)
+    ln = (I64 * len(lens))(*lens)
+    w = (P * len(wts))(*wts)
+    return LIB.r3d_joint_concat_permute_qknorm(ctypes.cast(arr, P), ctypes.cast(ln, P), len(ptrs),
+                                               None if null_w else ctypes.cast(w, P), eps, out, dtype, 1,
+                                               2, D, ctypes.byref(rope) if rope else None, None)
+
+
+def test_permute_qknorm_rejects():
+    W = 0x60000000
+    assert _permn([A, B_], [10, 5], [W, None], null_w=True) == -1
+    assert "norm weight array" in LIB.r3d_last_error().decode()
+    assert _permn([A, B_], [10, 5], [W, None], eps=-1.0) == -1 and "eps" in LIB.r3d_last_error().decode()
+    assert _permn([A, B_], [10, 5], [W, None], eps=float("nan")) == -1
+    assert _permn([A, B_], [10, 5], [W + 4, None]) == -1 and "aligned" in LIB.r3d_last_error().decode()
+    assert _permn([A, B_], [10, 5], [None, W], D=96) == -2 and "QK-norm" in LIB.r3d_last_error().decode()
+    assert _permn([A, B_], [10, 5], [None, O + 64]) == -1 and "norm weights" in LIB.r3d_last_error().decode()
+    # every plain-permute check still applies
+    assert _permn([A, None], [10, 5], [W, None]) == -1 and "segment 1" in LIB.r3d_last_error().decode()
 
 
 def test_lse_merge_rejects():

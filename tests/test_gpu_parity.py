@@ -140,6 +140,61 @@ def test_permute_with_fused_rope(gpu, dtype, D):
 
 
 # ------------------------------------------------------------------------------------------
+# QK-norm fused ahead of RoPE and the re-layout (r3d_joint_concat_permute_qknorm)
+# ------------------------------------------------------------------------------------------
+
+def check_prepared(got: torch.Tensor, ref: np.ndarray, dtype, what=""):
+    """got: GPU result [B,H,S,D]; ref: the oracle's values, already rounded to dtype."""
+    g = to_f64(got.cpu())
+    d = np.abs(g - ref)
+    exact = float((d == 0).mean())
+    if dtype == torch.bfloat16:
+        ulp = _bf16_ulp(ref)
+    else:
+        ax = np.abs(ref)
+        ulp = np.exp2(np.floor(np.log2(np.where(ax > 0, ax, 1.0))) - 23)
+    say(f"[{what}] exact fraction {exact:.6f}, max ulps {(d / ulp).max():.2f}")
+    assert (d <= ulp).all(), what
+    assert exact >= 0.999, what
+
+
+@pytest.mark.parametrize("dtype,D,grid,split,B,H,lens,normed,rope,mult", [
+    (torch.bfloat16, 128, (3, 6, 7), (32, 48, 48), 2, 3, (126, 19, 5), (0, 1, 2), True, 1.0),
+    (torch.float32, 64, (2, 8, 15), (16, 24, 24), 1, 4, (240, 13, 3), (0, 2), True, 1.0),
+    (torch.bfloat16, 64, (2, 2, 3), (16, 24, 24), 2, 5, (12, 7, 9), (1, 2), False, 1.0),
+    (torch.bfloat16, 128, (1, 4, 6), (0, 64, 64), 1, 24, (24, 3, 2), (0, 1, 2), True, 1e-3),  # ~eps scale
+    (torch.bfloat16, 128, (2, 3, 3), (32, 48, 48), 1, 2, (18, 0, 5), (0, 2), True, 50.0),
+])
+def test_permute_with_fused_qknorm(gpu, dtype, D, grid, split, B, H, lens, normed, rope, mult):
+    say(f"qknorm {dtype} D={D} B={B} H={H} lens={lens} normed={normed} rope={rope} mult={mult}")
+    segs = [_rand((B, n, H, D), dtype, 101 + i, mult) for i, n in enumerate(lens)]
+    g = torch.Generator().manual_seed(7)
+    wts = [(1.0 + 0.3 * torch.randn(H * D, generator=g)) if i in normed else None for i in range(len(lens))]
+    eps = 1e-6
+    out = r3d.joint_concat_permute([s.to(gpu) for s in segs], r3d.Rope3D(grid, split) if rope else None,
+                                   norm=[w.to(gpu) if w is not None else None for w in wts], eps=eps)
+    torch.cuda.synchronize()
+    io = "bf16" if dtype == torch.bfloat16 else "f32"
+    # Without RoPE, give the oracle a grid whose tokens all sit at w = 0 with the whole
+    # head dimension on the w axis: its rotation of segment 0 is then the exact identity.
+    ref, _, _ = oracle.prepare_qkv([to_f64(s) for s in segs], [to_f64(s) for s in segs],
+                                   [to_f64(s) for s in segs], grid if rope else (lens[0], 1, 1),
+                                   split if rope else (0, 0, D), 10000.0, io,
+                                   norm_q=[w.double().numpy() if w is not None else None for w in wts],
+                                   eps=eps)
+    if not rope and 0 not in normed:
+        np.testing.assert_array_equal(_bits(out)[:, :, :lens[0]],
+                                      oracle.joint_concat_permute([_bits(segs[0])]))
+    check_prepared(out, ref, dtype, "qknorm+rope" if rope else "qknorm")
+    off = 0
+    for i, n in enumerate(lens):  # segments without weights and rotation are bit-exact copies
+        if i != 0 and i not in normed and n > 0:
+            np.testing.assert_array_equal(_bits(out)[:, :, off:off + n],
+                                          oracle.joint_concat_permute([_bits(segs[i])]))
+        off += n
+
+
+# ------------------------------------------------------------------------------------------
 # attn_fwd on small shapes: full tensors
 # ------------------------------------------------------------------------------------------
 
