@@ -248,6 +248,26 @@ def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps
     res["attn_fwd_bshd"] = {"ms": round(ms, 4), "TFLOPs": round(w.attn_flops / (ms * 1e-3) / 1e12, 2)}
     log(f"attn_fwd_bshd: {ms:.3f} ms, {res['attn_fwd_bshd']['TFLOPs']:.1f} TFLOP/s")
     del obshd
+    # One rank's share of the sharded forms (P = 8), on this GPU: a Ulysses rank's H/P heads at
+    # the full sequence, and a CP/ring rank's S/P query rows against all keys with one kv_chunk
+    # per ring round.
+    P = 8
+    if w.H % P == 0 and w.S % P == 0:
+        hp, sp = w.H // P, w.S // P
+        qh, kh, vh = (t[:, :hp].contiguous() for t in (q, k, v))
+        ms = timed(lambda: r3d.attn_fwd(qh, kh, vh, scale=w.scale, kv_chunk=w.kv_chunk))
+        fl = 4.0 * w.B * hp * w.S * w.S * w.D
+        res["attn_fwd_ulysses_shard"] = {"ms": round(ms, 4), "H": hp, "S": w.S,
+                                         "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del qh, kh, vh
+        qs = q[:, :, :sp].contiguous()
+        ms = timed(lambda: r3d.attn_fwd(qs, k, v, scale=w.scale, kv_chunk=sp))
+        fl = 4.0 * w.B * w.H * sp * w.S * w.D
+        res["attn_fwd_cp_shard"] = {"ms": round(ms, 4), "Sq": sp, "Skv": w.S, "kv_chunk": sp,
+                                    "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 2)}
+        del qs
+        for kname in ("attn_fwd_ulysses_shard", "attn_fwd_cp_shard"):
+            log(f"{kname}: {res[kname]['ms']:.3f} ms, {res[kname]['TFLOPs']:.1f} TFLOP/s")
     return res
 
 

@@ -393,3 +393,42 @@ def test_workload_parity(gpu, w):
         got_out = out.reshape(-1, w.D)[torch.from_numpy(rows).to(gpu)]
         got_lse = lse.reshape(-1)[torch.from_numpy(rows).to(gpu)]
         check_attn(got_out, got_lse, ref_out, ref_lse, out.dtype, w.name)
+
+
+# ------------------------------------------------------------------------------------------
+# Shard shapes of the multi-GPU forms, on one GPU ("Context Parallelism in vLLM Omni Neuron",
+# §Ring attention / §Full K/V AllGather: rank r keeps S/P query rows against the full K/V;
+# xDiT PR #586, USP: a Ulysses rank holds all S tokens of H/P heads)
+# ------------------------------------------------------------------------------------------
+
+def test_shard_shape_proxies(gpu):
+    w = next(x for x in WORKLOADS if x.name == "pro-clip")
+    P, rank = 8, 3
+    say(f"shard proxies of {w.name}: P={P}, Ulysses H={w.H // P}, CP Sq={w.S // P}")
+    inp = make_inputs(w)
+    rope = r3d.Rope3D(w.grid, w.split, w.theta)
+    dev = {n: [s.to(gpu) for s in inp[n]] for n in "qkv"}
+    q = r3d.joint_concat_permute(dev["q"], rope)
+    k = r3d.joint_concat_permute(dev["k"], rope)
+    v = r3d.joint_concat_permute(dev["v"], None)
+    del dev
+    hp, sp = w.H // P, w.S // P
+    # Ulysses: the first rank's heads, full sequence; identical to the full call on those heads
+    full, full_lse = r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk)
+    uo, ul = r3d.attn_fwd(q[:, :hp].contiguous(), k[:, :hp].contiguous(), v[:, :hp].contiguous(),
+                          scale=w.scale, kv_chunk=w.kv_chunk)
+    assert torch.equal(uo, full[:, :hp]) and torch.equal(ul, full_lse[:, :hp])
+    del full, full_lse, uo, ul
+    # CP / ring: rank r's query rows against all keys, one kv_chunk per ring round
+    qs = q[:, :, rank * sp:(rank + 1) * sp].contiguous()
+    co, cl = r3d.attn_fwd(qs, k, v, scale=w.scale, kv_chunk=sp)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.prepare_qkv([to_f64(s) for s in inp["q"]], [to_f64(s) for s in inp["k"]],
+                                    [to_f64(s) for s in inp["v"]], w.grid, w.split, w.theta, "bf16")
+    rqs = np.ascontiguousarray(rq[:, :, rank * sp:(rank + 1) * sp])
+    g = np.random.default_rng(w.seed + 5)
+    rows = np.sort(g.choice(w.B * w.H * sp, size=48, replace=False))
+    ref_out, ref_lse = oracle.attention_rows(rqs, rk, rv, rows, w.scale)
+    idx = torch.from_numpy(rows).to(gpu)
+    check_attn(co.reshape(-1, w.D)[idx], cl.reshape(-1)[idx], ref_out, ref_lse, co.dtype,
+               f"CP shard Sq={sp} rank {rank}")
