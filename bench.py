@@ -247,6 +247,15 @@ def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps
                                     out_layout="bshd"))
     res["attn_fwd_bshd"] = {"ms": round(ms, 4), "TFLOPs": round(w.attn_flops / (ms * 1e-3) / 1e12, 2)}
     log(f"attn_fwd_bshd: {ms:.3f} ms, {res['attn_fwd_bshd']['TFLOPs']:.1f} TFLOP/s")
+    # the constant-max variant (Cauchy-Schwarz row bound; key-norm pre-pass included)
+    if w.dtype == "bf16":
+        ws = torch.empty(w.B * w.H, dtype=torch.float32, device=dev)
+        ms = timed(lambda: r3d.attn_fwd_constmax(q, k, v, scale=w.scale, out=obshd.view(q.shape), lse=lse,
+                                                 workspace=ws))
+        res["attn_fwd_constmax"] = {"ms": round(ms, 4),
+                                    "TFLOPs": round(w.attn_flops / (ms * 1e-3) / 1e12, 2)}
+        log(f"attn_fwd_constmax: {ms:.3f} ms, {res['attn_fwd_constmax']['TFLOPs']:.1f} TFLOP/s")
+        del ws
     del obshd
     # One rank's share of the sharded forms (P = 8), on this GPU: a Ulysses rank's H/P heads at
     # the full sequence, and a CP/ring rank's S/P query rows against all keys with one kv_chunk

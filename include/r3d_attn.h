@@ -174,6 +174,30 @@ R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void*
                               int64_t kv_chunk, int32_t dtype, void* stream);
 
 /*
+ * r3d_attn_fwd_constmax — r3d_attn_fwd (bf16, out [B, H, Sq, D]) whose softmax
+ * reference is a per-row bound fixed before any key is read instead of the
+ * running max: the kernel of "Context Parallelism in vLLM Omni Neuron",
+ * §Related information (ring_attention_const_max_fwd: "softmax max is a
+ * runtime bound"), where a known bound lets K/V chunks be consumed in any
+ * order with no rescaling — chunk partials simply add, no log-sum-exp merge.
+ * The bound is Cauchy-Schwarz:  m_i = |scale| |q_i| max_j |k_j|  >=  every
+ * logit of row i; max_j |k_j| per head is computed by a pre-pass into the
+ * workspace.  p = e^(s - m_i) <= 1, out = sum p v / sum p,
+ * lse = m_i + ln(sum p): the same function as r3d_attn_fwd while the bound
+ * exceeds the row's true max by less than about 87 (fp32's exponent range;
+ * beyond it every p of a row underflows and the row comes out NaN).
+ *   kmax_ws : DEVICE fp32 workspace of B*H values, 4-byte aligned, overlapping
+ *             nothing else; on return it holds max_j |k_j|^2 per (b, h).
+ *   dtype   : R3D_BF16 only.  Other arguments as r3d_attn_fwd (no kv_chunk:
+ *             with a fixed reference the chunking does not change the result).
+ * Errors: as r3d_attn_fwd, plus R3D_EINVAL for the workspace and
+ * R3D_EUNSUPPORTED for fp32.
+ */
+R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* kmax_ws, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                  float scale, int32_t dtype, void* stream);
+
+/*
  * r3d_lse_merge — combine n partial attention results of the same queries
  * against disjoint key sets (the ring-attention combine: each ring step
  * attends one K/V shard, "Context Parallelism in vLLM Omni Neuron",

@@ -247,11 +247,17 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
+// kConstMax: the softmax reference is a per-row bound fixed before any key is
+// read -- the Cauchy-Schwarz bound |scale| |q_i| max_j |k_j| >= every logit
+// of the row, from kmax2[bh] = max_j |k_j|^2 -- instead of the running max:
+// no max reduction, no rescale, and chunk partials simply add.  Exact as
+// long as the bound exceeds the row's true max by less than fp32's exponent
+// range (about 87 in natural-log units).
+template <int D, bool kConstMax>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
-    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd) {
+    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ kmax2) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
   __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
@@ -310,6 +316,19 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
   // Running state: acc (oacc), max m and per-lane partial sum l, log2 domain.
   float m_run = -INFINITY, l_run = 0.f;
+  if constexpr (kConstMax) {
+    // |q_i|^2 from the Q fragments (each lane half holds half of the row).
+    float qq = 0.f;
+#pragma unroll
+    for (int s = 0; s < G::kSteps; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)qf[s][e];
+        qq = fmaf(x, x, qq);
+      }
+    qq = sum_halves(qq);
+    m_run = c * sqrtf(qq * kmax2[bh]);  // the fixed reference, log2 units
+  }
 
   const int64_t first_cend = chunk < Skv ? chunk : Skv;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
@@ -385,12 +404,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       if (h2 == kSub) break;
 
       // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
-      float mx = sacc[0];
+      float m_use = m_run;
+      if constexpr (!kConstMax) {
+        float mx = sacc[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-      mx = max_halves(mx);
-      const float cand = mx * c;
-      const float m_use = (cand > m_run + kTau) ? cand : m_run;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = max_halves(mx);
+        const float cand = mx * c;
+        m_use = (cand > m_run + kTau) ? cand : m_run;
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
       // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       // Rescale last, and only when some row's reference moved (alpha is 0 on
       // a chunk's first step): acc already holds step h2-1's PV (issued above),
       // and step h2's PV comes after.
-      if (__ballot(m_use != m_run)) {
+      if (!kConstMax && __ballot(m_use != m_run)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         l_run *= alpha;
 #pragma unroll
@@ -435,7 +457,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     // normalise to (O, L) = (acc / l, m + log2 l), and let the next chunk
     // start from acc = O, m = L, l = 1 -- value O at weight 2^L.  The next
     // chunk's online rescale then forms exactly O 2^(L - L') + O_c 2^(lse_c - L').
-    if (chunk_done) {
+    if (!kConstMax && chunk_done) {
       const float l_tot = sum_halves(l_run);
       const float inv = 1.0f / l_tot;
 #pragma unroll
@@ -460,6 +482,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     }
   }
 
+  if constexpr (kConstMax) {  // one sum over all keys: normalise now
+    const float l_tot = sum_halves(l_run);
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
+    m_run += log2f(l_tot);
+  }
+
   // ---- epilogue: out (bf16, RNE) and lse (natural log) ----
   // The last tile closed a chunk, so acc = O and m = L (log2).
   // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
@@ -480,11 +510,54 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   }
 }
 
-}  // namespace
+// kmax2[bh] = 0, so that the partial maxima below can be combined by atomic
+// max on the bit patterns of non-negative floats (ordered like the values).
+__global__ void zero_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                            int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                            bool out_bshd, hipStream_t stream) {
+// kmax2[bh] = max_j |k_j|^2 over the head's Skv key rows.  Grid (B*H) x
+// kSplit blocks; block (bh, part) scans rows part, part + kSplit*rows_per_pass
+// ...; kCpr consecutive lanes hold one row's 16-byte chunks.
+constexpr int kNormThreads = 256;
+constexpr int kNormSplit = 64;
+template <int D>
+__global__ __launch_bounds__(kNormThreads) void key_norm_max_kernel(const uint16_t* __restrict__ k,
+                                                                    float* __restrict__ kmax2, int64_t Skv) {
+  constexpr int kCpr = D / 8;
+  constexpr int kRows = kNormThreads / kCpr;  // rows per block pass
+  const int64_t bh = blockIdx.x / kNormSplit;
+  const int part = blockIdx.x % kNormSplit;
+  const int t = threadIdx.x, r = t / kCpr, ci = t % kCpr;
+  const uint16_t* kb = k + bh * Skv * D;
+  float best = 0.f;
+  for (int64_t j = (int64_t)part * kRows + r; j < Skv; j += (int64_t)kNormSplit * kRows) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(kb + j * D + ci * 8);
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = __uint_as_float(x[w] << 16), b = __uint_as_float(x[w] & 0xffff0000u);
+      ss = fmaf(a, a, fmaf(b, b, ss));
+    }
+#pragma unroll
+    for (int o = kCpr / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    best = fmaxf(best, ss);
+  }
+  __shared__ float red[kNormThreads];
+  red[t] = best;
+  __syncthreads();
+  for (int sz = kNormThreads / 2; sz > 0; sz >>= 1) {
+    if (t < sz) red[t] = fmaxf(red[t], red[t + sz]);
+    __syncthreads();
+  }
+  if (t == 0) atomicMax(reinterpret_cast<unsigned int*>(kmax2 + bh), __float_as_uint(red[0]));
+}
+
+template <bool kConstMax>
+hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                 int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
+                                 bool out_bshd, float* kmax2, hipStream_t stream) {
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
   const int n_blocks = (int)(B * H * n_qt);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
@@ -493,13 +566,36 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
   auto* op = static_cast<uint16_t*>(out);
+  if constexpr (kConstMax) {
+    const int64_t nbh = B * H;
+    zero_kernel<<<(unsigned)((nbh + 255) / 256), 256, 0, stream>>>(kmax2, nbh);
+    if (D == 64)
+      key_norm_max_kernel<64><<<(unsigned)(nbh * kNormSplit), kNormThreads, 0, stream>>>(kp, kmax2, Skv);
+    else
+      key_norm_max_kernel<128><<<(unsigned)(nbh * kNormSplit), kNormThreads, 0, stream>>>(kp, kmax2, Skv);
+  }
   if (D == 64)
-    attn_bf16_kernel<64><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk,
-                                                             n_qt, n_blocks, out_bshd ? 1 : 0);
+    attn_bf16_kernel<64, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
+        qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2);
   else
-    attn_bf16_kernel<128><<<n_blocks, kThreads, 0, stream>>>(qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk,
-                                                              n_qt, n_blocks, out_bshd ? 1 : 0);
+    attn_bf16_kernel<128, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
+        qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                            int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
+                            bool out_bshd, hipStream_t stream) {
+  return launch_attn_bf16_impl<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, nullptr,
+                                      stream);
+}
+
+hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                     float scale, hipStream_t stream) {
+  return launch_attn_bf16_impl<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, kmax2, stream);
 }
 
 }  // namespace r3d

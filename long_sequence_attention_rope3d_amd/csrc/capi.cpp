@@ -273,6 +273,43 @@ R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void*
   return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, true, stream);
 }
 
+R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
+                                  float* kmax_ws, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                  float scale, int32_t dtype, void* stream) {
+  if (dtype != R3D_BF16) return fail(R3D_EUNSUPPORTED, "attn_fwd_constmax: bf16 only");
+  if (!kmax_ws || ((uintptr_t)kmax_ws & 3)) return fail(R3D_EINVAL, "attn_fwd_constmax: workspace NULL or misaligned");
+  // q/k/v/out/lse are validated as in r3d_attn_fwd, the workspace on top.
+  if (!q || !k || !v || !out) return fail(R3D_EINVAL, "attn_fwd: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(R3D_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
+    return fail(R3D_EINVAL, "attn_fwd: B, H, Sq, Skv, D must be > 0");
+  if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
+  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
+  int64_t nq, nk, bhq, nbh;
+  if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
+    return fail(R3D_EINVAL, "attn_fwd: tensor too large");
+  product(bhq, {B, H, Sq});
+  product(nbh, {B, H});
+  if (!launch_fits(B * H * ((Sq + 127) / 128), 256) || !launch_fits(nbh * 64, 256))
+    return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
+  const int es = 2;
+  const void* ins[3] = {q, k, v};
+  const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(out, nq * es, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: out overlaps an input");
+    if (lse && overlap(lse, bhq * 4, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: lse overlaps an input");
+    if (overlap(kmax_ws, nbh * 4, ins[i], in_bytes[i]))
+      return fail(R3D_EINVAL, "attn_fwd_constmax: workspace overlaps an input");
+  }
+  if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "attn_fwd: lse overlaps out");
+  if (overlap(kmax_ws, nbh * 4, out, nq * es) || (lse && overlap(kmax_ws, nbh * 4, lse, bhq * 4)))
+    return fail(R3D_EINVAL, "attn_fwd_constmax: workspace overlaps an output");
+  return hip_status(r3d::launch_attn_bf16_constmax(q, k, v, out, lse, kmax_ws, B, H, Sq, Skv, D, scale,
+                                                   (hipStream_t)stream),
+                    "attn_fwd_constmax");
+}
+
 R3D_API int r3d_lse_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,
                           int32_t parts_dtype, void* out, float* lse_out, int32_t out_dtype,
                           int64_t B, int64_t H, int64_t S, int64_t D, void* stream) {

@@ -48,6 +48,12 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                             int64_t kv_chunk, bool out_bshd, hipStream_t stream);
 
+// attn_fwd with a constant per-row softmax reference (the Cauchy-Schwarz
+// bound from the head's largest key norm); kmax2 is a [B*H] fp32 workspace.
+hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
+                                     float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                     float scale, hipStream_t stream);
+
 // attn_fwd, fp32 path (D = 64 or 128); out_bshd as above.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,

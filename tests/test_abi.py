@@ -30,7 +30,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute",
                                   "r3d_joint_concat_permute_qknorm", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
-                                  "r3d_lse_merge", "r3d_last_error", "r3d_version"])
+                                  "r3d_attn_fwd_constmax", "r3d_lse_merge", "r3d_last_error",
+                                  "r3d_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -57,6 +58,7 @@ I32, I64 = ctypes.c_int32, ctypes.c_int64
 F = ctypes.c_float
 LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P]
 LIB.r3d_attn_fwd_bshd.argtypes = LIB.r3d_attn_fwd.argtypes
+LIB.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, F, I32, P]
 LIB.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute_qknorm.argtypes = [P, P, I32, P, ctypes.c_double, P, I32, I64, I64, I64, P, P]
@@ -92,6 +94,18 @@ def _attn(fn="r3d_attn_fwd", **kw):
 def test_attn_fwd_rejects(fn, kw, status, needle):
     assert _attn(fn, **kw) == status
     assert needle in LIB.r3d_last_error().decode()
+
+
+def test_attn_fwd_constmax_rejects():
+    W = 0x70000000
+    def call(ws=W, dtype=1, D=128, out=O):
+        return LIB.r3d_attn_fwd_constmax(A, B_, C, out, L_, ws, 1, 2, 64, 64, D, 0.125, dtype, None)
+    assert call(dtype=0) == -2 and "bf16" in LIB.r3d_last_error().decode()
+    assert call(ws=None) == -1 and "workspace" in LIB.r3d_last_error().decode()
+    assert call(ws=W + 2) == -1
+    assert call(ws=O + 64) == -1 and "overlaps" in LIB.r3d_last_error().decode()
+    assert call(D=96) == -2
+    assert call(out=A) == -1
 
 
 class Rope(ctypes.Structure):

@@ -432,3 +432,98 @@ def test_shard_shape_proxies(gpu):
     idx = torch.from_numpy(rows).to(gpu)
     check_attn(co.reshape(-1, w.D)[idx], cl.reshape(-1)[idx], ref_out, ref_lse, co.dtype,
                f"CP shard Sq={sp} rank {rank}")
+
+
+# ------------------------------------------------------------------------------------------
+# Constant-max variant (r3d_attn_fwd_constmax): the softmax reference is the Cauchy-Schwarz
+# bound |scale| |q_i| max_j |k_j| fixed per row ("Context Parallelism in vLLM Omni Neuron",
+# §Related information: ring_attention_const_max_fwd), the same function as attn_fwd
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D,B,H,Sq,Skv,sm", [
+    (128, 1, 2, 300, 333, 1.0),
+    (128, 1, 1, 200, 5000, 3.0),     # sharp softmax
+    (128, 1, 1, 64, 300, 0.0),       # scale 0: uniform
+    (128, 1, 1, 64, 300, -1.0),      # negative scale
+    (128, 2, 3, 385, 129, 1.0),
+    (64, 2, 3, 130, 257, 1.0),
+    (64, 1, 1, 1, 1, 1.0),
+])
+def test_attn_constmax_small(gpu, D, B, H, Sq, Skv, sm):
+    scale = sm / math.sqrt(D)
+    say(f"constmax D={D} B={B} H={H} Sq={Sq} Skv={Skv} sm={sm}")
+    q = _rand((B, H, Sq, D), torch.bfloat16, 111)
+    k = _rand((B, H, Skv, D), torch.bfloat16, 112)
+    v = _rand((B, H, Skv, D), torch.bfloat16, 113)
+    ws = torch.empty(B * H, dtype=torch.float32, device=gpu)
+    out, lse = r3d.attn_fwd_constmax(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
+    check_attn(out, lse, ref_out, ref_lse, torch.bfloat16, f"constmax {D} {Sq}x{Skv} sm={sm}")
+    # the workspace holds max_j |k_j|^2 per head
+    kk = to_f64(k)
+    want = (kk * kk).sum(-1).max(-1).reshape(-1)
+    np.testing.assert_allclose(ws.cpu().double().numpy(), want, rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["lite-clip", "image-dit", "pro-clip"])
+def test_attn_constmax_workloads(gpu, name):
+    w = next(x for x in WORKLOADS if x.name == name)
+    say(f"constmax workload {w.name}: S={w.S} H={w.H}")
+    inp = make_inputs(w)
+    rope = r3d.Rope3D(w.grid, w.split, w.theta)
+    dev = {n: [s.to(gpu) for s in inp[n]] for n in "qkv"}
+    q = r3d.joint_concat_permute(dev["q"], rope)
+    k = r3d.joint_concat_permute(dev["k"], rope)
+    v = r3d.joint_concat_permute(dev["v"], None)
+    del dev
+    out, lse = r3d.attn_fwd_constmax(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.prepare_qkv([to_f64(s) for s in inp["q"]], [to_f64(s) for s in inp["k"]],
+                                    [to_f64(s) for s in inp["v"]], w.grid, w.split, w.theta, "bf16")
+    rows = sample_rows(w)
+    ref_out, ref_lse = oracle.attention_rows(rq, rk, rv, rows, w.scale)
+    idx = torch.from_numpy(rows).to(gpu)
+    check_attn(out.reshape(-1, w.D)[idx], lse.reshape(-1)[idx], ref_out, ref_lse, out.dtype,
+               f"constmax {w.name}")
+
+
+def test_attn_constmax_outlier_gate(gpu):
+    """The gate on the outlier workload (1% of keys at 8x): the Cauchy-Schwarz bound can exceed
+    a row's true max by more than fp32's exponent range, and then all of that row's p underflow.
+    Rows whose bound gap is comfortably inside the range must be right; rows beyond it are the
+    non-finite ones.  (The default path, attn_fwd's online max, passes this workload.)"""
+    w = next(x for x in WORKLOADS if x.name == "long-video")
+    inp = make_inputs(w)
+    rope = r3d.Rope3D(w.grid, w.split, w.theta)
+    dev = {n: [s.to(gpu) for s in inp[n]] for n in "qkv"}
+    q = r3d.joint_concat_permute(dev["q"], rope)
+    k = r3d.joint_concat_permute(dev["k"], rope)
+    v = r3d.joint_concat_permute(dev["v"], None)
+    del dev
+    out, lse = r3d.attn_fwd_constmax(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.prepare_qkv([to_f64(s) for s in inp["q"]], [to_f64(s) for s in inp["k"]],
+                                    [to_f64(s) for s in inp["v"]], w.grid, w.split, w.theta, "bf16")
+    g = np.random.default_rng(w.seed + 9)
+    rows = np.sort(g.choice(w.B * w.H * w.S, size=64, replace=False))
+    ref_out, ref_lse = oracle.attention_rows(rq, rk, rv, rows, w.scale)
+    qf = rq.reshape(-1, w.D)[rows]
+    heads = (rows // w.S) % w.H
+    kh = rk.reshape(w.B * w.H, w.S, w.D)
+    knorm = np.sqrt((kh * kh).sum(-1)).max(-1)                       # per head
+    gap = np.empty(rows.size)
+    for i, (qq, hh) in enumerate(zip(qf, heads)):
+        smax = (kh[hh] @ qq).max() * w.scale
+        gap[i] = abs(w.scale) * np.sqrt(qq @ qq) * knorm[hh] - smax
+    got_out = out.reshape(-1, w.D)[torch.from_numpy(rows).to(gpu)].cpu().double().numpy()
+    got_lse = lse.reshape(-1)[torch.from_numpy(rows).to(gpu)].cpu().double().numpy()
+    finite = np.isfinite(got_out).all(1) & np.isfinite(got_lse)
+    say(f"bound gap (nats): min {gap.min():.1f} median {np.median(gap):.1f} max {gap.max():.1f}; "
+        f"{(~finite).sum()} of {rows.size} sampled rows non-finite")
+    ok = gap < 75.0
+    assert ok.any()
+    assert finite[ok].all()
+    d = np.abs(got_out[ok] - ref_out[ok])
+    assert d.max() <= BF16_MAX_ABS and np.abs(got_lse[ok] - ref_lse[ok]).max() <= LSE_ABS
+    assert not finite[gap > 88.0].any()        # past fp32's range every p of the row is 0
