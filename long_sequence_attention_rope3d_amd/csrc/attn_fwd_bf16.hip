@@ -150,10 +150,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum): one v_maximum3_f32
+// per two new operands, with no quieting of the inputs first (fmaxf's
+// maxNum needs a canonicalising v_max x, x per operand).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // x of this lane combined with x of lane l^32.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -314,8 +319,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   f32x16 oacc[G::kDBlk];
 #pragma unroll
   for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
-  // Running state: acc (oacc), max m and per-lane partial sum l, log2 domain.
-  float m_run = -INFINITY, l_run = 0.f;
+  // Running state: acc (oacc), max m and per-lane partial sum l, log2 domain;
+  // thr = (m + kTau) / c, the raw logit above which the reference must move.
+  float m_run = -INFINITY, l_run = 0.f, thr = -INFINITY;
+  const float inv_c = 1.0f / c;
   if constexpr (kConstMax) {
     // |q_i|^2 from the Q fragments (each lane half holds half of the row).
     float qq = 0.f;
@@ -404,14 +411,21 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       if (h2 == kSub) break;
 
       // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
+      // The row max is compared in raw logit units against thr, so the
+      // common step (no row moves) spends one compare; only a step in which
+      // some row's max exceeds its threshold forms the new reference.
       float m_use = m_run;
+      bool moved = false;  // wave-uniform
       if constexpr (!kConstMax) {
         float mx = sacc[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        for (int i = 1; i < 16; ++i) mx = vmax(mx, sacc[i]);
         mx = max_halves(mx);
-        const float cand = mx * c;
-        m_use = (cand > m_run + kTau) ? cand : m_run;
+        const bool up = mx > thr;
+        if (__builtin_expect(__ballot(up) != 0, 0)) {
+          m_use = up ? mx * c : m_run;
+          moved = true;
+        }
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
@@ -437,14 +451,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       // Rescale last, and only when some row's reference moved (alpha is 0 on
       // a chunk's first step): acc already holds step h2-1's PV (issued above),
       // and step h2's PV comes after.
-      if (!kConstMax && __ballot(m_use != m_run)) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      if (!kConstMax && moved) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 where the row kept it
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
+        m_run = m_use;
+        thr = (m_run + kTau) * inv_c;
       }
       l_run += ps;
-      m_run = m_use;
     }
 
     if (kStages == 3 && issue)
@@ -463,6 +478,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 #pragma unroll
       for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
       m_run += log2f(l_tot);
+      thr = (m_run + kTau) * inv_c;
       l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
     }
     cur.advance(chunk, Skv);
