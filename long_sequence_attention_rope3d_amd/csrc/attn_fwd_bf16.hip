@@ -96,6 +96,7 @@ constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
 constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+constexpr float kSlack = 32.0f;   // bound slack under which the row max is skipped, log2 units
 
 template <int D>
 struct Geom {
@@ -252,12 +253,23 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// kConstMax: the softmax reference is a per-row bound fixed before any key is
-// read -- the Cauchy-Schwarz bound |scale| |q_i| max_j |k_j| >= every logit
-// of the row, from kmax2[bh] = max_j |k_j|^2 -- instead of the running max:
-// no max reduction, no rescale, and chunk partials simply add.  Exact as
-// long as the bound exceeds the row's true max by less than fp32's exponent
-// range (about 87 in natural-log units).
+// Both variants read kmax2[bh] = max_j |k_j|^2 over the head's keys, which
+// gives each row the Cauchy-Schwarz bound bnd = c |q_i| max_j |k_j| >= every
+// logit of the row (log2 units).
+//
+// Online (kConstMax false): the reference m is an attained value -- a step's
+// row max, or a chunk's log-sum-exp after the merge -- as in the plain online
+// softmax, but the 16-element row max is only formed while bnd > m + kSlack
+// for some row of the wave.  Once m is within kSlack of the bound, no later
+// logit can exceed it by more than kSlack, so p = 2^(s c - m) <= 2^kSlack
+// without looking at the step's values; only rows whose bound is loose (or
+// the first step, m = -inf) pay for the max.  The result is the online
+// softmax's for every input: the reference only sets the scale of acc and l.
+//
+// kConstMax: the reference is the bound itself, fixed before any key is read:
+// no max reduction, no rescale, and chunk partials simply add.  Exact as long
+// as the bound exceeds the row's true max by less than fp32's exponent range
+// (about 87 in natural-log units); opt-in.
 template <int D, bool kConstMax>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -319,12 +331,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   f32x16 oacc[G::kDBlk];
 #pragma unroll
   for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
-  // Running state: acc (oacc), max m and per-lane partial sum l, log2 domain;
-  // thr = (m + kTau) / c, the raw logit above which the reference must move.
+  // Running state: acc (oacc), reference m and per-lane partial sum l, log2
+  // domain; thr = (m + kTau) / c, the raw logit above which the reference
+  // must move while the row max is being formed.
   float m_run = -INFINITY, l_run = 0.f, thr = -INFINITY;
   const float inv_c = 1.0f / c;
-  if constexpr (kConstMax) {
-    // |q_i|^2 from the Q fragments (each lane half holds half of the row).
+  // The row's logit bound: |q_i|^2 from the Q fragments (each lane half holds
+  // half of the row) times max_j |k_j|^2.
+  float bnd;
+  {
     float qq = 0.f;
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s)
@@ -334,8 +349,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         qq = fmaf(x, x, qq);
       }
     qq = sum_halves(qq);
-    m_run = c * sqrtf(qq * kmax2[bh]);  // the fixed reference, log2 units
+    bnd = c * sqrtf(qq * kmax2[bh]);
   }
+  if constexpr (kConstMax) m_run = bnd;  // the fixed reference
+  // Wave-uniform: some row of the wave still needs its row max formed.
+  bool need_max = true;
+  auto update_need_max = [&]() { need_max = __ballot(bnd > m_run + kSlack) != 0; };
 
   const int64_t first_cend = chunk < Skv ? chunk : Skv;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       // some row's max exceeds its threshold forms the new reference.
       float m_use = m_run;
       bool moved = false;  // wave-uniform
-      if constexpr (!kConstMax) {
+      if (!kConstMax && need_max) {
         float mx = sacc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = vmax(mx, sacc[i]);
@@ -458,6 +477,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
         m_run = m_use;
         thr = (m_run + kTau) * inv_c;
+        update_need_max();
       }
       l_run += ps;
     }
@@ -479,6 +499,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
       m_run += log2f(l_tot);
       thr = (m_run + kTau) * inv_c;
+      update_need_max();
       l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
     }
     cur.advance(chunk, Skv);
@@ -582,7 +603,7 @@ hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, vo
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
   auto* op = static_cast<uint16_t*>(out);
-  if constexpr (kConstMax) {
+  {
     const int64_t nbh = B * H;
     zero_kernel<<<(unsigned)((nbh + 255) / 256), 256, 0, stream>>>(kmax2, nbh);
     if (D == 64)
@@ -601,10 +622,10 @@ hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, vo
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                            int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                            bool out_bshd, hipStream_t stream) {
-  return launch_attn_bf16_impl<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, nullptr,
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, float* kmax2,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                            int64_t kv_chunk, bool out_bshd, hipStream_t stream) {
+  return launch_attn_bf16_impl<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, kmax2,
                                       stream);
 }
 

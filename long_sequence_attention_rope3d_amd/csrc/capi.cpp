@@ -5,10 +5,14 @@
 // supported head dims, non-overlap).  No exception crosses the ABI.
 #include "r3d_attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "launch.h"
 
@@ -222,6 +226,35 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
 }
 
 namespace {
+// Library-owned device workspace of the bf16 attention path (the per-head
+// largest squared key norm, B*H floats): one buffer per (device, stream), so
+// calls on one stream use it in stream order and calls on different streams
+// never share it.  Allocated on the first call on a stream and grown when a
+// call needs more heads (after that stream has drained the old buffer); kept
+// until the process ends.
+hipError_t head_workspace(hipStream_t stream, int64_t n, float** ws) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<float*, int64_t>> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& slot = cache[{dev, stream}];
+  if (slot.second < n) {
+    if (slot.first) {
+      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
+      if ((e = hipFree(slot.first)) != hipSuccess) return e;
+      slot = {nullptr, 0};
+    }
+    const int64_t cap = std::max<int64_t>(n, 4096);
+    void* p = nullptr;
+    if ((e = hipMalloc(&p, (size_t)cap * sizeof(float))) != hipSuccess) return e;
+    slot = {static_cast<float*>(p), cap};
+  }
+  *ws = slot.first;
+  return hipSuccess;
+}
+
 // Shared by both output layouts: the validation is identical (out has the
 // same number of elements either way).
 int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
@@ -252,9 +285,13 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "attn_fwd: lse overlaps out");
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   hipError_t e;
-  if (dtype == R3D_BF16)
-    e = r3d::launch_attn_bf16(q, k, v, out, lse, B, H, Sq, Skv, D, scale, chunk, out_bshd, (hipStream_t)stream);
-  else
+  if (dtype == R3D_BF16) {
+    float* ws = nullptr;
+    e = head_workspace((hipStream_t)stream, B * H, &ws);
+    if (e == hipSuccess)
+      e = r3d::launch_attn_bf16(q, k, v, out, lse, ws, B, H, Sq, Skv, D, scale, chunk, out_bshd,
+                                (hipStream_t)stream);
+  } else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
                              D, scale, chunk, out_bshd, (hipStream_t)stream);
   return hip_status(e, "attn_fwd");

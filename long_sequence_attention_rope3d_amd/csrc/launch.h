@@ -43,10 +43,11 @@ hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, 
                           int64_t D, const RopeArgs& rope, hipStream_t stream);
 
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
-// instead of [B, H, Sq, D].
+// instead of [B, H, Sq, D].  kmax2 is a [B*H] fp32 device workspace (the
+// per-head largest squared key norm, written and read on `stream`).
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
-                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                            int64_t kv_chunk, bool out_bshd, hipStream_t stream);
+                            float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                            float scale, int64_t kv_chunk, bool out_bshd, hipStream_t stream);
 
 // attn_fwd with a constant per-row softmax reference (the Cauchy-Schwarz
 // bound from the head's largest key norm); kmax2 is a [B*H] fp32 workspace.

@@ -233,6 +233,41 @@ def test_attn_fwd_small(gpu, case):
     check_attn(out, lse, ref_out, ref_lse, dtype, str(case))
 
 
+@pytest.mark.parametrize("D,gap,kv_chunk", [
+    (128, 28.0, 0), (128, 28.0, 256), (128, 40.0, 0), (128, 40.0, 300), (128, 0.0, 300),
+    (64, 28.0, 128), (64, 45.0, 0),
+])
+def test_attn_bound_gated_max(gpu, D, gap, kv_chunk):
+    """The bf16 kernel forms a row's max only while the row's Cauchy-Schwarz bound
+    c |q| max_j |k_j| exceeds its reference by more than a fixed slack (32 in log2 units).
+    Half of the rows point along one direction u with |q| = 10; key 3 is b1*u and key 700 is
+    b2*u, so those rows' reference after the first step is c*10*b1 and their bound is
+    c*10*b2, `gap` log2 units higher.  gap 28: the max is skipped and key 700 arrives with
+    p ~ 2^28; gap 40: the max is formed and the reference moves at key 700; gap 0: the bound
+    is attained at key 3.  The other rows (|q| ~ 0.3, random direction) sit in the other
+    regime in the same waves.  Every case must match the oracle."""
+    B, H, Sq, Skv = 1, 2, 200, 1000
+    scale = 1.0 / math.sqrt(D)
+    c = scale / math.log(2.0)
+    g = torch.Generator().manual_seed(1000 + D + int(gap) + kv_chunk)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u /= u.norm()
+    a = 10.0
+    q = 0.3 * torch.randn(B, H, Sq, D, generator=g, dtype=torch.float64) / math.sqrt(D)
+    q[:, :, : Sq // 2] = a * u + 0.01 * torch.randn(B, H, Sq // 2, D, generator=g, dtype=torch.float64)
+    k = 0.05 * torch.randn(B, H, Skv, D, generator=g, dtype=torch.float64)
+    b1 = 5.0
+    b2 = b1 + gap / (c * a)
+    k[:, :, 3] = b1 * u
+    k[:, :, 700] = b2 * u
+    v = torch.randn(B, H, Skv, D, generator=g, dtype=torch.float64)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
+    check_attn(out, lse, ref_out, ref_lse, torch.bfloat16, f"D={D} gap={gap} kv_chunk={kv_chunk}")
+
+
 def test_attn_fwd_without_lse(gpu):
     q = _rand((1, 2, 150, 128), torch.bfloat16, 51).to(gpu)
     k = _rand((1, 2, 190, 128), torch.bfloat16, 52).to(gpu)
