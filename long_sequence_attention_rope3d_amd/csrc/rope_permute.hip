@@ -89,11 +89,13 @@ __device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const double2* cs, int ch
 
 // QK-norm of one 16-byte chunk, then (cs != nullptr) its rotation: every
 // element x becomes x * r * w (r = 1/sqrt(mean square + eps) of its token,
-// w its channel's weight, `w` pointing at the chunk's first channel), the
-// pairs are rotated, all in fp64, and each value is rounded once.
+// w its channel's weight: wa, wb hold the chunk's channels 0..7, fp32 rows
+// use wa only), the pairs are rotated, all in fp64, and each value is
+// rounded once.
 template <bool BF16>
-__device__ __forceinline__ u32x4 norm_rotate_chunk(u32x4 v, double r, const float* w, const double2* cs,
+__device__ __forceinline__ u32x4 norm_rotate_chunk(u32x4 v, double r, float4 wa, float4 wb, const double2* cs,
                                                    int chunk) {
+  const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
   if constexpr (BF16) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -203,6 +205,14 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
     const int epc = 16 / (BF16 ? 2 : 4);  // elements per 16-byte chunk
     const float* wn = nullptr;
     double r = 1.0;
+    const int h0 = threadIdx.x / per_h;
+    // With a norm, the thread's first kHold chunks (heads h0, h0 + hstep, ...)
+    // are loaded once, all in flight together, summed, and kept in registers
+    // for the normalise / rotate / store pass; heads beyond them (only for
+    // H > kHold * hstep) are read again from L2.
+    constexpr int kHold = NORM ? 16 : 1;
+    u32x4 held[kHold];
+    const int nh = (valid && H > h0) ? (H - h0 + hstep - 1) / hstep : 0;  // this thread's heads
     if constexpr (NORM) {
       // Pass 1: the token's sum of squares over all H*D values.  The threads
       // of token tl are slots tl*cpr + [0, cpr) of each of the hstep head
@@ -210,7 +220,13 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
       wn = valid ? segs.norm_w[seg] : nullptr;
       double ss = 0.0;
       if (wn) {
-        for (int h = threadIdx.x / per_h; h < H; h += hstep) ss += chunk_sumsq<BF16>(src[(int64_t)h * cpr]);
+#pragma unroll
+        for (int i = 0; i < kHold; ++i)
+          if (i < nh) held[i] = src[(int64_t)(h0 + i * hstep) * cpr];
+#pragma unroll
+        for (int i = 0; i < kHold; ++i)
+          if (i < nh) ss += chunk_sumsq<BF16>(held[i]);
+        for (int h = h0 + kHold * hstep; h < H; h += hstep) ss += chunk_sumsq<BF16>(src[(int64_t)h * cpr]);
       }
       red[threadIdx.x] = ss;
       __syncthreads();
@@ -224,20 +240,45 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
       if (!valid) return;
       r = rnorm[tl];
     }
-    // Pass 2 (the only pass without NORM): normalise / rotate / copy.  With a
-    // norm the rows are read a second time, from the L2 the first pass filled.
-#pragma unroll 4
-    for (int h = threadIdx.x / per_h; h < H; h += hstep) {
-      u32x4 v;
-      if (NORM && wn) {
-        v = src[(int64_t)h * cpr];
-        v = norm_rotate_chunk<BF16>(v, r, wn + (int64_t)h * D + chunk * epc, rot ? cs[tl] : nullptr, chunk);
-      } else {
-        v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
-        if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
-      }
+    auto store = [&](int h, u32x4 v) {
       const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
       __builtin_nontemporal_store(v, dst + o);
+    };
+    if (NORM && wn) {
+      // Pass 2 with a norm: from the registers, then the re-read tail.  The
+      // chunk's weights (epc fp32 values, 16-byte aligned) are loaded one
+      // head ahead, before the previous head's store, so their L2 latency
+      // overlaps the arithmetic.
+      auto wload = [&](int h, float4& a, float4& c) {
+        const float4* wp = reinterpret_cast<const float4*>(wn + (int64_t)h * D + chunk * epc);
+        a = wp[0];
+        c = BF16 ? wp[1] : a;
+      };
+      float4 wa = {}, wb = {};
+      if (nh > 0) wload(h0, wa, wb);
+#pragma unroll
+      for (int i = 0; i < kHold; ++i) {
+        if (i < nh) {
+          const int h = h0 + i * hstep;
+          float4 na = wa, nb = wb;
+          if (i + 1 < nh) wload(h + hstep, na, nb);
+          store(h, norm_rotate_chunk<BF16>(held[i], r, wa, wb, rot ? cs[tl] : nullptr, chunk));
+          wa = na;
+          wb = nb;
+        }
+      }
+      for (int h = h0 + kHold * hstep; h < H; h += hstep) {
+        wload(h, wa, wb);
+        store(h, norm_rotate_chunk<BF16>(src[(int64_t)h * cpr], r, wa, wb, rot ? cs[tl] : nullptr, chunk));
+      }
+    } else {
+      // Copy / rotate (the only pass without a norm).
+#pragma unroll 4
+      for (int h = h0; h < H; h += hstep) {
+        u32x4 v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
+        if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+        store(h, v);
+      }
     }
   } else {
     // Generic row widths (no RoPE: any D whose row is a multiple of 16 bytes).
