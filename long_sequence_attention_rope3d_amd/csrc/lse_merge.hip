@@ -53,15 +53,46 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__
   const int c = (int)(gid - row * cpr);
   if (row >= rows) return;
 
+  // The first kHeld parts' lse values are loaded together and kept in
+  // registers (indices are compile-time, predicated on n, which is uniform);
+  // parts beyond them (n > kHeld) are read again as needed.
+  constexpr int kHeld = 16, kG = 4;
+  float lv[kHeld];
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) lv[j] = j < n ? lse_parts[(int64_t)j * rows + row] : -INFINITY;
   float hi = -INFINITY;
-  for (int i = 0; i < n; ++i) hi = fmaxf(hi, lse_parts[(int64_t)i * rows + row]);
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) hi = fmaxf(hi, lv[j]);
+  for (int i = kHeld; i < n; ++i) hi = fmaxf(hi, lse_parts[(int64_t)i * rows + row]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
   if (hi != -INFINITY) {
     float sum = 0.f;
-    for (int i = 0; i < n; ++i) sum += expf(lse_parts[(int64_t)i * rows + row] - hi);
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j)
+      if (j < n) sum += expf(lv[j] - hi);
+    for (int i = kHeld; i < n; ++i) sum += expf(lse_parts[(int64_t)i * rows + row] - hi);
     L = hi + logf(sum);
-    for (int i = 0; i < n; ++i) {
+    // Data in groups of kG parts: a group's loads are all issued before any
+    // is used, so several parts are in flight per thread.
+#pragma unroll
+    for (int g = 0; g < kHeld; g += kG) {
+      if (g < n) {
+        float x[kG][8];
+#pragma unroll
+        for (int j = 0; j < kG; ++j)
+          if (g + j < n) load8<PBF16>(parts, ((int64_t)(g + j) * rows + row) * D + c * 8, x[j]);
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+          if (g + j < n) {
+            const float w = expf(lv[g + j] - L);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[j][e], acc[e]);
+          }
+        }
+      }
+    }
+    for (int i = kHeld; i < n; ++i) {
       const float w = expf(lse_parts[(int64_t)i * rows + row] - L);
       float x[8];
       load8<PBF16>(parts, ((int64_t)i * rows + row) * D + c * 8, x);

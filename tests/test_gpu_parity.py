@@ -348,14 +348,19 @@ def test_attn_fwd_kv_permutation_invariance(gpu):
 # lse_merge
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("parts_dtype,out_dtype", [(torch.float32, torch.bfloat16),
-                                                   (torch.bfloat16, torch.bfloat16),
-                                                   (torch.float32, torch.float32)])
-def test_lse_merge_matches_oracle(gpu, parts_dtype, out_dtype):
-    n, B, H, S, D = 5, 1, 3, 77, 128
+@pytest.mark.parametrize("parts_dtype,out_dtype,n", [(torch.float32, torch.bfloat16, 5),
+                                                     (torch.bfloat16, torch.bfloat16, 5),
+                                                     (torch.float32, torch.float32, 5),
+                                                     (torch.float32, torch.float32, 1),
+                                                     (torch.float32, torch.float32, 16),
+                                                     (torch.bfloat16, torch.float32, 21)])
+def test_lse_merge_matches_oracle(gpu, parts_dtype, out_dtype, n):
+    """n = 1, 5 (a partial group of four), 16 (every lse held in registers) and 21 (five
+    parts past the held ones, read by the fallback loop)."""
+    B, H, S, D = 1, 3, 77, 128
     parts = _rand((n, B, H, S, D), parts_dtype, 81)
     lse = _rand((n, B, H, S), torch.float32, 82, 3.0)
-    lse[1, 0, 0, :10] = -math.inf
+    lse[n // 2, 0, 0, :10] = -math.inf
     lse[:, 0, 1, 5] = -math.inf          # a row with no keys at all
     out, L = r3d.lse_merge(parts.to(gpu), lse.to(gpu), out_dtype=out_dtype)
     ref_out, ref_L = oracle.lse_merge(to_f64(parts), to_f64(lse))
