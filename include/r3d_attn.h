@@ -150,12 +150,20 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  *   D   : 64 or 128.  dtype R3D_BF16 runs on bf16 MFMA with fp32 accumulation and an
  *         fp32 softmax (P rounded to bf16 for the PV product); R3D_F32 is an all-fp32
  *         path.
- * Memory: the R3D_BF16 path keeps a small library-owned device workspace (B*H
- * floats: each head's largest squared key norm, from which every row gets a
- * Cauchy-Schwarz bound on its logits), one per (current device, stream).  The
- * first call on a stream, or a call with more heads than any before on it,
+ * Key split: an R3D_BF16 launch whose query tiles leave the GPU's compute
+ *   units mostly idle (fewer tiles than an eighth of them, or a last round of
+ *   tiles at most a quarter full) splits every tile's keys into up to 8 ranges
+ *   of whole chunks (whole 128-key tiles with one chunk), runs each range as
+ *   its own block, and merges the fp32 partials (O, lse) with the lse_merge
+ *   kernel -- the ring's per-shard partial + merge, on one device.  The result
+ *   equals the unsplit one up to rounding.  r3d_attn_fwd_bshd never splits.
+ * Memory: the R3D_BF16 path keeps library-owned device workspaces, one per
+ * (current device, stream, kind): B*H floats (each head's largest squared key
+ * norm, from which every row gets a Cauchy-Schwarz bound on its logits) and,
+ * for split launches, n_split*B*H*Sq*(D+1) floats of partials.  The first call
+ * on a stream that needs one, or a call that needs more than any before on it,
  * allocates it with hipMalloc (after synchronizing that stream when it grows);
- * later calls allocate nothing.  Calls on one stream reuse it in stream order.
+ * later calls allocate nothing.  Calls on one stream reuse them in stream order.
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
  * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype), R3D_EHIP.
  */

@@ -273,21 +273,30 @@ __device__ __forceinline__ void wait_vm_barrier() {
 template <int D, bool kConstMax>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
-    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ kmax2) {
+    void* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
+    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ kmax2,
+    int n_split, int64_t split_len, int out_f32) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
   __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t st1_k[G::kTile], st1_v[G::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t st2_k[G::kTile], st2_v[G::kTile];
 
-  // Block -> (head, query tile): XCD x runs logical tiles [x*per + min(x, rem), ...).
+  // Block -> (head, key split, query tile): XCD x runs logical tiles
+  // [x*per + min(x, rem), ...), and consecutive logical tiles are consecutive
+  // query tiles of one (head, split), which stream the same keys.
   const int bid = blockIdx.x;
   const int per = n_blocks / kXcds, rem = n_blocks % kXcds;
   const int xcd = bid % kXcds, slot = bid / kXcds;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int64_t bh = logical / n_qt;
-  const int qt = logical - (int)bh * n_qt;
+  const int hs = logical / n_qt;  // head * n_split + split
+  const int qt = logical - hs * n_qt;
+  const int64_t bh = hs / n_split;
+  const int split = hs - (int)bh * n_split;
+  // This block's keys: [kv_begin, kv_end), a whole number of chunks (or, with
+  // one chunk, of tiles); n_split = 1 is the whole sequence.
+  const int64_t kv_begin = (int64_t)split * split_len;
+  const int64_t kv_end = kv_begin + split_len < Skv ? kv_begin + split_len : Skv;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -356,9 +365,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   bool need_max = true;
   auto update_need_max = [&]() { need_max = __ballot(bnd > m_run + kSlack) != 0; };
 
-  const int64_t first_cend = chunk < Skv ? chunk : Skv;
+  const int64_t first_cend = kv_begin + chunk < kv_end ? kv_begin + chunk : kv_end;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
-  TileCursor pf{0, first_cend};
+  TileCursor pf{kv_begin, first_cend};
   // Copy tile pf into stage P (K and V), then advance pf.
   auto copy = [&](auto stage) {
     constexpr int P = decltype(stage)::value;
@@ -374,10 +383,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       dma_tile<D, false, false>(lk, ks, n, wave, lane);
       dma_tile<D, true, false>(lv, vs, n, wave, lane);
     }
-    pf.advance(chunk, Skv);
+    pf.advance(chunk, kv_end);
   };
   copy(std::integral_constant<int, 0>{});
-  if (kStages == 3 && pf.kv0 < Skv) copy(std::integral_constant<int, 1>{});
+  if (kStages == 3 && pf.kv0 < kv_end) copy(std::integral_constant<int, 1>{});
   // The prologue tiles target different LDS objects, so their DMAs may be
   // issued in either order: wait for all of them once.
   wait_vm_barrier<0>();
@@ -385,12 +394,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   // One tile of n keys in stage S: prefetch the tile after next into stage
   // (S+2)%3, consume stage S, then wait for the next tile (this wave's part of
   // it) and meet at the barrier.
-  TileCursor cur{0, first_cend};  // the tile being consumed
+  TileCursor cur{kv_begin, first_cend};  // the tile being consumed
   auto step = [&](auto stage) {
     constexpr int S = decltype(stage)::value;
     const int n = cur.n();
     const bool chunk_done = cur.kv0 + n == cur.cend;
-    const bool issue = pf.kv0 < Skv;
+    const bool issue = pf.kv0 < kv_end;
     if (issue) copy(std::integral_constant<int, (S + kStages - 1) % kStages>{});  // the tile kStages-1 ahead
 
     const char* kt = reinterpret_cast<const char*>(S == 0 ? st0_k : S == 1 ? st1_k : st2_k);
@@ -502,7 +511,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       update_need_max();
       l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
     }
-    cur.advance(chunk, Skv);
+    cur.advance(chunk, kv_end);
   };
 
   // Tiles run through the stages in a straight line; a chunk's last tile ends
@@ -510,12 +519,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   // alpha = 0 clears acc and l.
   for (;;) {
     step(std::integral_constant<int, 0>{});
-    if (cur.kv0 >= Skv) break;
+    if (cur.kv0 >= kv_end) break;
     step(std::integral_constant<int, 1>{});
-    if (cur.kv0 >= Skv) break;
+    if (cur.kv0 >= kv_end) break;
     if constexpr (kStages == 3) {
       step(std::integral_constant<int, 2>{});
-      if (cur.kv0 >= Skv) break;
+      if (cur.kv0 >= kv_end) break;
     }
   }
 
@@ -527,23 +536,36 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     m_run += log2f(l_tot);
   }
 
-  // ---- epilogue: out (bf16, RNE) and lse (natural log) ----
+  // ---- epilogue: out (bf16, RNE; or fp32 for a key-split partial) and lse (natural log) ----
   // The last tile closed a chunk, so acc = O and m = L (log2).
   // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
   if (qrow < Sq) {
-    // out row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major).
+    // Row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major); a
+    // split partial goes to [n_split, B*H*Sq, D] (lse [n_split, B*H*Sq]).
     const int64_t b = bh / H;
-    const int64_t orow = out_bshd ? (b * Sq + qrow) * H + (bh - b * H) : bh * Sq + qrow;
-    uint16_t* op = out + orow * D;
+    const int64_t nbh = (int64_t)n_blocks / ((int64_t)n_split * n_qt);  // B*H
+    const int64_t prow = ((int64_t)split * nbh + bh) * Sq + qrow;
+    if (out_f32) {
+      float* op = static_cast<float*>(out) + prow * D;
 #pragma unroll
-    for (int b = 0; b < G::kDBlk; ++b)
+      for (int b = 0; b < G::kDBlk; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = u32x2{pack_bf16(oacc[b][4 * g], oacc[b][4 * g + 1]),
-                              pack_bf16(oacc[b][4 * g + 2], oacc[b][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * hf) = w;
-      }
-    if (lse && hf == 0) lse[bh * Sq + qrow] = m_run * 0.69314718055994530942f;
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(op + 32 * b + 8 * g + 4 * hf) =
+              make_float4(oacc[b][4 * g], oacc[b][4 * g + 1], oacc[b][4 * g + 2], oacc[b][4 * g + 3]);
+    } else {
+      const int64_t orow = out_bshd ? (b * Sq + qrow) * H + (bh - b * H) : prow;
+      uint16_t* op = static_cast<uint16_t*>(out) + orow * D;
+#pragma unroll
+      for (int b = 0; b < G::kDBlk; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = u32x2{pack_bf16(oacc[b][4 * g], oacc[b][4 * g + 1]),
+                                pack_bf16(oacc[b][4 * g + 2], oacc[b][4 * g + 3])};
+          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * hf) = w;
+        }
+    }
+    if (lse && hf == 0) lse[prow] = m_run * 0.69314718055994530942f;
   }
 }
 
@@ -594,15 +616,15 @@ __global__ __launch_bounds__(kNormThreads) void key_norm_max_kernel(const uint16
 template <bool kConstMax>
 hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
                                  int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                                 bool out_bshd, float* kmax2, hipStream_t stream) {
+                                 bool out_bshd, float* kmax2, int n_split, int64_t split_len, bool out_f32,
+                                 hipStream_t stream) {
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
-  const int n_blocks = (int)(B * H * n_qt);
+  const int n_blocks = (int)(B * H * n_split * n_qt);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
   const auto* qp = static_cast<const uint16_t*>(q);
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
-  auto* op = static_cast<uint16_t*>(out);
   {
     const int64_t nbh = B * H;
     zero_kernel<<<(unsigned)((nbh + 255) / 256), 256, 0, stream>>>(kmax2, nbh);
@@ -613,26 +635,68 @@ hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, vo
   }
   if (D == 64)
     attn_bf16_kernel<64, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2, n_split,
+        split_len, out_f32 ? 1 : 0);
   else
     attn_bf16_kernel<128, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, op, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2, n_split,
+        split_len, out_f32 ? 1 : 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
+                        int64_t* split_len) {
+  *split_len = Skv;
+  const int64_t n_qt = (Sq + kBM - 1) / kBM;
+  const int64_t blocks = B * H * n_qt;
+  if (n_cus <= 0 || blocks >= 4 * (int64_t)n_cus) return 1;  // the last round is a small share already
+  // Split only a grid that leaves the CUs mostly idle: under an eighth of
+  // them, or a last round at most a quarter full.  (Measured: a last round
+  // filled 55-70% costs less than its share -- the chip is power-limited and
+  // clocks up when fewer CUs run -- and splitting such grids was 1-10% slower
+  // or no faster, while the merge adds traffic.)
+  const int64_t last = blocks % n_cus;
+  if (!(blocks * 8 < n_cus || (last != 0 && last * 4 <= n_cus))) return 1;
+  // Split unit: a chunk when there are several, else a tile; at least 1024 keys per split.
+  const int64_t unit = kv_chunk < Skv ? kv_chunk : kBN;
+  const int64_t n_units = (Skv + unit - 1) / unit;
+  auto eff = [&](int64_t nb) {  // busy share of the CU rounds that nb equal blocks take
+    const int64_t rounds = (nb + n_cus - 1) / n_cus;
+    return (double)nb / (double)(rounds * n_cus);
+  };
+  int best = 1;
+  int64_t best_len = Skv;
+  double best_eff = eff(blocks);
+  for (int s = 2; s <= kMaxKeySplit; ++s) {
+    const int64_t len = ((n_units + s - 1) / s) * unit;
+    if (len < 1024) break;
+    const int64_t n = (Skv + len - 1) / len;  // splits actually made
+    const double e = eff(blocks * n);
+    if (e > best_eff + 0.05) {
+      best = (int)n;
+      best_len = len;
+      best_eff = e;
+    }
+  }
+  *split_len = best_len;
+  return best;
+}
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, float* kmax2,
                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                            int64_t kv_chunk, bool out_bshd, hipStream_t stream) {
+                            int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len, bool out_f32,
+                            hipStream_t stream) {
   return launch_attn_bf16_impl<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, kmax2,
-                                      stream);
+                                      n_split, split_len, out_f32, stream);
 }
 
 hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
                                      float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                                      float scale, hipStream_t stream) {
-  return launch_attn_bf16_impl<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, kmax2, stream);
+  return launch_attn_bf16_impl<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, kmax2, 1, Skv, false,
+                                     stream);
 }
 
 }  // namespace r3d

@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 #include "launch.h"
@@ -226,33 +227,50 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
 }
 
 namespace {
-// Library-owned device workspace of the bf16 attention path (the per-head
-// largest squared key norm, B*H floats): one buffer per (device, stream), so
-// calls on one stream use it in stream order and calls on different streams
-// never share it.  Allocated on the first call on a stream and grown when a
-// call needs more heads (after that stream has drained the old buffer); kept
-// until the process ends.
-hipError_t head_workspace(hipStream_t stream, int64_t n, float** ws) {
+// Library-owned device workspaces of the bf16 attention path, one buffer per
+// (device, stream, kind), so calls on one stream use them in stream order and
+// calls on different streams never share one.  Kinds: kHeadNorms, the
+// per-head largest squared key norm (B*H floats, for the bound-gated max);
+// kSplitParts, the fp32 partials (O, lse) of a key-split launch.  Allocated
+// on first use and grown when a call needs more (after that stream has
+// drained the old buffer); kept until the process ends.
+enum WsKind { kHeadNorms = 0, kSplitParts = 1 };
+hipError_t stream_workspace(hipStream_t stream, WsKind kind, size_t bytes, void** ws) {
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<float*, int64_t>> cache;
+  static std::map<std::tuple<int, hipStream_t, int>, std::pair<void*, size_t>> cache;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  auto& slot = cache[{dev, stream}];
-  if (slot.second < n) {
+  auto& slot = cache[{dev, stream, (int)kind}];
+  if (slot.second < bytes) {
     if (slot.first) {
       if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
       if ((e = hipFree(slot.first)) != hipSuccess) return e;
       slot = {nullptr, 0};
     }
-    const int64_t cap = std::max<int64_t>(n, 4096);
+    const size_t cap = std::max<size_t>(bytes, 16384);
     void* p = nullptr;
-    if ((e = hipMalloc(&p, (size_t)cap * sizeof(float))) != hipSuccess) return e;
-    slot = {static_cast<float*>(p), cap};
+    if ((e = hipMalloc(&p, cap)) != hipSuccess) return e;
+    slot = {p, cap};
   }
   *ws = slot.first;
   return hipSuccess;
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cus.find(dev);
+  if (it != cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cus[dev] = n;
+  return n;
 }
 
 // Shared by both output layouts: the validation is identical (out has the
@@ -286,11 +304,28 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   hipError_t e;
   if (dtype == R3D_BF16) {
-    float* ws = nullptr;
-    e = head_workspace((hipStream_t)stream, B * H, &ws);
-    if (e == hipSuccess)
-      e = r3d::launch_attn_bf16(q, k, v, out, lse, ws, B, H, Sq, Skv, D, scale, chunk, out_bshd,
-                                (hipStream_t)stream);
+    const hipStream_t st = (hipStream_t)stream;
+    void* norms = nullptr;
+    e = stream_workspace(st, kHeadNorms, (size_t)(B * H) * sizeof(float), &norms);
+    // Few query tiles (a shard's shape): split the keys over several blocks per
+    // tile and merge the fp32 partials, so the grid fills the CUs.
+    int64_t split_len = Skv;
+    const int n_split = out_bshd ? 1 : r3d::attn_bf16_key_split(B, H, Sq, Skv, chunk, device_cus(), &split_len);
+    if (e == hipSuccess && n_split > 1) {
+      const int64_t rows = bhq;
+      void* parts = nullptr;
+      e = stream_workspace(st, kSplitParts, (size_t)(n_split * rows * (D + 1)) * sizeof(float), &parts);
+      if (e == hipSuccess) {
+        float* o_parts = static_cast<float*>(parts);
+        float* l_parts = o_parts + n_split * rows * D;
+        e = r3d::launch_attn_bf16(q, k, v, o_parts, l_parts, static_cast<float*>(norms), B, H, Sq, Skv, D, scale,
+                                  chunk, false, n_split, split_len, true, st);
+        if (e == hipSuccess) e = r3d::launch_lse_merge(o_parts, l_parts, n_split, false, out, lse, true, rows, D, st);
+      }
+    } else if (e == hipSuccess) {
+      e = r3d::launch_attn_bf16(q, k, v, out, lse, static_cast<float*>(norms), B, H, Sq, Skv, D, scale, chunk,
+                                out_bshd, 1, Skv, false, st);
+    }
   } else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
                              D, scale, chunk, out_bshd, (hipStream_t)stream);

@@ -45,9 +45,22 @@ hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, 
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
 // instead of [B, H, Sq, D].  kmax2 is a [B*H] fp32 device workspace (the
 // per-head largest squared key norm, written and read on `stream`).
+// n_split > 1: the keys are split into n_split ranges of split_len keys (a
+// multiple of kv_chunk, or of the 128-key tile when kv_chunk >= Skv), each
+// query tile runs once per range, and out / lse receive the fp32 partials
+// [n_split, B*H*Sq, D] / [n_split, B*H*Sq] (out_f32 true, out_bshd false),
+// for an lse_merge over the n_split parts.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                             float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                            float scale, int64_t kv_chunk, bool out_bshd, hipStream_t stream);
+                            float scale, int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len,
+                            bool out_f32, hipStream_t stream);
+
+// Number of key splits (1: none) for a bf16 attention launch on a device with
+// n_cus compute units, and *split_len: splitting only when the query tiles
+// alone leave the last round of blocks on the CUs mostly empty.
+constexpr int kMaxKeySplit = 8;
+int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
+                        int64_t* split_len);
 
 // attn_fwd with a constant per-row softmax reference (the Cauchy-Schwarz
 // bound from the head's largest key norm); kmax2 is a [B*H] fp32 workspace.
