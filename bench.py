@@ -42,15 +42,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_code_sha256(path: str) -> str:
+    """sha256 of a source file's code: '//' comments, trailing blanks and empty
+    lines removed, so that editing a comment does not count as a kernel change."""
+    lines = []
+    for line in open(path, encoding="utf-8").read().splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def _traffic_for_current_kernel():
     """HBM bytes per attn_fwd launch from the committed rocprofv3 --pmc summary,
-    or None if there is none or the kernel source changed since it was taken."""
+    or None if there is none or the kernel code changed since it was taken."""
     try:
         text = open(TRAFFIC_FILE).read()
-        src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        src_hash = kernel_code_sha256(ATTN_SRC)
     except OSError:
         return None
-    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_hash = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
         return None

@@ -20,6 +20,11 @@
 //     (§Memory and Compute Benefits: the split keeps full attention quality).
 // The softmax runs in the log2 domain: logits are multiplied by
 // c = |scale| * log2(e) inside one FMA, so p = 2^(s*c - m).
+// A launch whose query tiles leave the CUs mostly idle can also split each
+// tile's keys into ranges of whole chunks run by separate blocks; each then
+// writes its fp32 partial (O, lse) and the ranges are combined by the same
+// log-sum-exp merge in a second kernel (lse_merge.hip) -- ring attention's
+// per-shard partials, with the shards as blocks of one launch.
 //
 // Mapping onto CDNA4
 // ------------------
@@ -29,9 +34,10 @@
 //   wave at 168 registers (the kernel needs ~166 and spills nothing).  384
 //   also divides the 52608-token workload exactly, and 137 query tiles per
 //   head keep the last round of blocks on the CUs nearly full.
-// * Grid = B*H*ceil(Sq/384) blocks, re-numbered so consecutive query tiles of
-//   one head land on the same XCD (hardware hands block i to XCD i % 8): the
-//   CUs of an XCD stream the same K/V and share it in that XCD's L2.
+// * Grid = B*H*n_split*ceil(Sq/384) blocks, re-numbered so consecutive query
+//   tiles of one (head, key range) land on the same XCD (hardware hands block
+//   i to XCD i % 8): the CUs of an XCD stream the same K/V and share it in
+//   that XCD's L2.
 // * K/V tiles of kBN = 128 keys are copied global -> LDS by DMA
 //   (global_load_lds_dwordx4) into two stage buffers, row-major [key][d],
 //   with the 16-byte chunks of every row XOR-swizzled so that the operand
@@ -58,6 +64,10 @@
 //   it by more than kTau (log2 units); otherwise p = 2^(s*c - m) <= 2^kTau and
 //   acc keeps its scale.  The result is unchanged (the same m scales both
 //   acc and l); most steps skip the 64-register rescale of acc.
+// * Bound-gated max: the row max itself is only formed while some row of the
+//   wave has a Cauchy-Schwarz logit bound more than kSlack above its
+//   reference (see the kernel's comment); on typical inputs that is the
+//   first step, and later steps spend no VALU work on the max at all.
 // * The row sum l adds the fp32 p before their bf16 rounding for the PV
 //   product, so lse keeps fp32 accuracy.
 #include <type_traits>

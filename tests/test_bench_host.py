@@ -1,0 +1,44 @@
+"""Host-side logic of bench.py (no GPU): the kernel-code hash that decides whether the
+committed HBM-traffic profile still describes the current attention kernel."""
+import importlib.util
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        spec.loader.exec_module(mod)
+    finally:
+        sys.argv = argv
+    return mod
+
+
+def test_kernel_code_hash_ignores_comments_but_not_code(tmp_path):
+    b = _bench()
+    base = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    p = tmp_path / "k.hip"
+    p.write_text(base)
+    h0 = b.kernel_code_sha256(str(p))
+    p.write_text("// a new header comment\n\n" + base.replace("// add one", "// increment"))
+    assert b.kernel_code_sha256(str(p)) == h0
+    p.write_text(base.replace("x + 1", "x + 2"))
+    assert b.kernel_code_sha256(str(p)) != h0
+
+
+def test_traffic_is_null_when_the_recorded_hash_differs(tmp_path, monkeypatch):
+    b = _bench()
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }\n")
+    prof = tmp_path / "traffic.md"
+    prof.write_text(f"kernel_code_sha256: {b.kernel_code_sha256(str(src))}\nhbm_bytes_per_launch: 1.5e+09\n")
+    monkeypatch.setattr(b, "ATTN_SRC", str(src))
+    monkeypatch.setattr(b, "TRAFFIC_FILE", str(prof))
+    assert b._traffic_for_current_kernel() == 1.5e9
+    src.write_text("int f() { return 2; }\n")
+    assert b._traffic_for_current_kernel() is None
