@@ -289,6 +289,9 @@ def test_attn_key_split_small(gpu, D, B, H, Sq, Skv, kv_chunk):
     ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
     check_attn(out, lse, ref_out, ref_lse, torch.bfloat16, f"split D={D} Skv={Skv} kv_chunk={kv_chunk}")
     check_attn(ob.transpose(1, 2), lb, ref_out, ref_lse, torch.bfloat16, "unsplit bshd")
+    # Without an lse output the merge still weighs the parts by their (workspace) lse.
+    o2 = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk, return_lse=False)
+    assert torch.equal(o2, out)
 
 
 def test_attn_fwd_without_lse(gpu):
