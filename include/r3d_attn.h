@@ -164,6 +164,9 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  * on a stream that needs one, or a call that needs more than any before on it,
  * allocates it with hipMalloc (after synchronizing that stream when it grows);
  * later calls allocate nothing.  Calls on one stream reuse them in stream order.
+ * Under HIP graph capture make one uncaptured call of the same or larger sizes
+ * on that stream first, so that the captured call needs no allocation (a
+ * growth inside capture fails with R3D_EHIP).
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
  * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype), R3D_EHIP.
  */
