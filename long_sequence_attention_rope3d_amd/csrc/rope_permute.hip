@@ -39,6 +39,8 @@ constexpr int kThreads = 256;
 constexpr int kTok = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Correctly rounded binary64 -> bfloat16 (round to nearest, ties to even).
 // bfloat16 keeps 8 significant bits, so for |y| >= 2^-126 the binary64
@@ -62,6 +64,24 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
   return ((f & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : (f >> 16);
 }
 
+// Two binary64 values -> two bfloat16 (y0 in the low half), each rounded
+// to nearest-even exactly as f64_to_bf16 does, mostly in hardware: RNE to
+// binary32 (v_cvt_f32_f64), then the packed binary32 -> bfloat16 RNE
+// (v_cvt_pk_bf16_f32).  bfloat16 midpoints are binary32 values and rounding
+// is monotonic, so the first rounding keeps y on its side of every midpoint;
+// the pair of roundings can differ from one rounding only when the first
+// lands exactly on a midpoint (low 16 bits 0x8000) without being exact --
+// or in the binary32 subnormal range.  Lanes meeting either case take
+// f64_to_bf16 (rare; a branch per call).
+__device__ __forceinline__ uint32_t f64x2_to_bf16x2(double y0, double y1) {
+  const float f0 = (float)y0, f1 = (float)y1;
+  const uint32_t u0 = __float_as_uint(f0), u1 = __float_as_uint(f1);
+  const bool slow = ((u0 & 0xffffu) == 0x8000u) | ((u1 & 0xffffu) == 0x8000u) | ((u0 & 0x7f800000u) == 0u) |
+                    ((u1 & 0x7f800000u) == 0u);
+  if (__builtin_expect(slow, 0)) return f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{f0, f1}, bf16x2_t));
+}
+
 // Rotates the pairs held in one 16-byte chunk.  Pair p of the row is
 // (x[2p], x[2p+1]); its (cos, sin) is cs[p].  The rotation is done in fp64
 // and rounded once to the storage type.
@@ -73,7 +93,7 @@ __device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const double2* cs, int ch
       const double2 c = cs[chunk * 4 + w];
       const double x0 = (double)__uint_as_float(v[w] << 16);
       const double x1 = (double)__uint_as_float(v[w] & 0xffff0000u);
-      v[w] = f64_to_bf16(x0 * c.x - x1 * c.y) | (f64_to_bf16(x0 * c.y + x1 * c.x) << 16);
+      v[w] = f64x2_to_bf16x2(x0 * c.x - x1 * c.y, x0 * c.y + x1 * c.x);
     }
   } else {
 #pragma unroll
@@ -107,7 +127,7 @@ __device__ __forceinline__ u32x4 norm_rotate_chunk(u32x4 v, double r, float4 wa,
         x0 = y0;
         x1 = y1;
       }
-      v[q] = f64_to_bf16(x0) | (f64_to_bf16(x1) << 16);
+      v[q] = f64x2_to_bf16x2(x0, x1);
     }
   } else {
 #pragma unroll
