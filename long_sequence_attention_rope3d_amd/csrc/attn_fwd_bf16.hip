@@ -60,10 +60,13 @@
 //   b16 values), two reads per 8-key fragment.  The O^T accumulator again
 //   holds one query per lane, so rescales and the chunk merge are per-lane
 //   scalars.
-// * Lazy rescale: the running max is only raised when a step's max exceeds
-//   it by more than kTau (log2 units); otherwise p = 2^(s*c - m) <= 2^kTau and
-//   acc keeps its scale.  The result is unchanged (the same m scales both
-//   acc and l); most steps skip the 64-register rescale of acc.
+// * Rescale only on a new maximum: when the row max is formed, the reference
+//   moves to it as soon as a step's max exceeds it (kTau = 0), so a row's
+//   largest logit gets p = 2^0 = 1, exact in bf16, and a row dominated by one
+//   key carries no rounding of that key's weight; steps whose max does not
+//   exceed the reference skip the 64-register rescale of acc.  (A lazy
+//   threshold of 8 was no faster and doubled the worst output error on rows
+//   dominated by one outlier key.)
 // * Bound-gated max: the row max itself is only formed while some row of the
 //   wave has a Cauchy-Schwarz logit bound more than kSlack above its
 //   reference (see the kernel's comment); on typical inputs that is the
@@ -105,7 +108,7 @@ static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
-constexpr float kTau = 8.0f;      // lazy-rescale threshold, log2 units
+constexpr float kTau = 0.0f;      // rescale threshold, log2 units (0: on every new maximum)
 constexpr float kSlack = 32.0f;   // bound slack under which the row max is skipped, log2 units
 
 template <int D>
