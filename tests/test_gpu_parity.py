@@ -452,8 +452,16 @@ def test_workload_parity(gpu, w):
     if w.S * w.S * w.H <= 256 * 256 * 2:
         ref_out, ref_lse = oracle.attention(rq, rk, rv, w.scale)
         check_attn(out, lse, ref_out, ref_lse, out.dtype, w.name)
+    elif w.S * w.S * w.H <= 5e8:
+        # every output element (lite-clip, image-dit: seconds of oracle time)
+        rows = np.arange(w.B * w.H * w.S, dtype=np.int64)
+        say(f"  all {rows.size} rows")
+        ref_out, ref_lse = oracle.attention_rows(rq, rk, rv, rows, w.scale)
+        check_attn(out.reshape(-1, w.D), lse.reshape(-1), ref_out, ref_lse, out.dtype, w.name)
     else:
         rows = sample_rows(w)
+        if w.S <= 60000:  # pro-clip: also every 4th row of head 0
+            rows = np.union1d(rows, np.arange(0, w.S, 4, dtype=np.int64))
         say(f"  {rows.size} sampled rows")
         ref_out, ref_lse = oracle.attention_rows(rq, rk, rv, rows, w.scale)
         got_out = out.reshape(-1, w.D)[torch.from_numpy(rows).to(gpu)]
