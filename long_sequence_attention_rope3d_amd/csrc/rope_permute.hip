@@ -16,12 +16,12 @@
 //                          RoPE, same page, §Self-Attention with Context
 //                          Parallelism).
 //
-// Layout of the work.  A block owns kTok consecutive tokens of one batch row
-// and all H heads of them.  Per token, the cos/sin of its D/2 pair angles are
+// Layout of the work.  A block owns kTok (with the QK-norm kTokNorm)
+// consecutive tokens of one batch row and all H heads of them.  Per token, the cos/sin of its D/2 pair angles are
 // computed once into LDS and reused by all H heads (angles depend only on
 // the token).  Each thread then moves 16-byte chunks: a thread keeps one
 // (token, chunk) slot and walks the heads, so for a fixed head the block
-// reads one contiguous 256-byte row per token and writes kTok contiguous
+// reads one contiguous 256-byte row per token and writes that many contiguous
 // rows of the [B, H, S, D] output — both sides are full-line, coalesced
 // accesses, and no LDS transpose is needed (the re-layout moves whole
 // D-rows).  Copies are bit-exact.  Angles, sin/cos and the rotation are
@@ -37,6 +37,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTok = 8;
+// With the QK-norm a block takes 4 tokens, so that each thread holds only a
+// few of its token's chunks (kHold) through the norm's reduction: the kernel
+// then fits 6 waves per SIMD instead of 4, and the latency of the
+// load -> reduce -> store sequence is hidden by more blocks in flight.
+constexpr int kTokNorm = 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -175,11 +180,13 @@ __device__ __forceinline__ double chunk_sumsq(u32x4 v) {
 template <bool BF16, bool PERMUTE, bool ROPE, bool NORM>
 __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, void* out,
                                                                 int H, int D, int64_t n_tb, RopeArgs rope) {
-  __shared__ double2 cs[kTok][kMaxPairs];
-  __shared__ double red[NORM ? kThreads : 1];
-  __shared__ double rnorm[kTok];
+  constexpr int kT = NORM ? kTokNorm : kTok;  // tokens per block
+  __shared__ double2 cs[kT][kMaxPairs];
+  // Norm partial sums, one per (head group, token): hstep * kT = kThreads / cpr
+  // of them, and cpr >= 8 for the row widths the norm accepts.
+  __shared__ double red[NORM ? kThreads / 8 : 1];
   const int64_t b = (int64_t)blockIdx.x / n_tb;
-  const int64_t tok0 = ((int64_t)blockIdx.x - b * n_tb) * kTok;
+  const int64_t tok0 = ((int64_t)blockIdx.x - b * n_tb) * kT;
   const int64_t S = segs.S;
   const int npairs = D / 2;
   const int cpr = D * (BF16 ? 2 : 4) / 16;  // 16-byte chunks per row
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
   if constexpr (ROPE) {
     // Token n of the video segment sits at (t, h, w), n = (t*gh + h)*gw + w.
     const int64_t nv = segs.len[0];
-    for (int e = threadIdx.x; e < kTok * npairs; e += kThreads) {
+    for (int e = threadIdx.x; e < kT * npairs; e += kThreads) {
       const int tl = e / npairs, p = e - tl * npairs;
       const int64_t s = tok0 + tl;
       double sn = 0.0, c = 1.0;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
     __syncthreads();
   }
 
-  const int per_h = kTok * cpr;
+  const int per_h = kT * cpr;
   // (The host allows NORM only for D in {64, 128}, which always takes this branch.)
   if (NORM || (per_h <= kThreads && kThreads % per_h == 0)) {
     // Each thread keeps one (token, chunk) slot and walks the heads.
@@ -230,13 +237,15 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
     // are loaded once, all in flight together, summed, and kept in registers
     // for the normalise / rotate / store pass; heads beyond them (only for
     // H > kHold * hstep) are read again from L2.
-    constexpr int kHold = NORM ? 16 : 1;
+    constexpr int kHold = NORM ? 6 : 1;  // all of them for bf16, D = 128, H <= 24
     u32x4 held[kHold];
     const int nh = (valid && H > h0) ? (H - h0 + hstep - 1) / hstep : 0;  // this thread's heads
     if constexpr (NORM) {
-      // Pass 1: the token's sum of squares over all H*D values.  The threads
-      // of token tl are slots tl*cpr + [0, cpr) of each of the hstep head
-      // groups; their partial sums meet in LDS.
+      // Pass 1: the token's sum of squares over all H*D values.  The cpr
+      // threads of token tl in each of the hstep head groups are consecutive
+      // lanes of one wave: they reduce by butterfly shuffles, and the group
+      // partials meet in LDS behind one barrier; every thread then forms its
+      // token's r itself.
       wn = valid ? segs.norm_w[seg] : nullptr;
       double ss = 0.0;
       if (wn) {
@@ -248,17 +257,13 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
           if (i < nh) ss += chunk_sumsq<BF16>(held[i]);
         for (int h = h0 + kHold * hstep; h < H; h += hstep) ss += chunk_sumsq<BF16>(src[(int64_t)h * cpr]);
       }
-      red[threadIdx.x] = ss;
-      __syncthreads();
-      if (threadIdx.x < kTok) {
-        double t = 0.0;
-        for (int g = 0; g < hstep; ++g)
-          for (int c = 0; c < cpr; ++c) t += red[g * per_h + threadIdx.x * cpr + c];
-        rnorm[threadIdx.x] = 1.0 / sqrt(t / (double)((int64_t)H * D) + segs.norm_eps);
-      }
+      for (int m = cpr / 2; m > 0; m >>= 1) ss += __shfl_xor(ss, m, cpr);
+      if (chunk == 0) red[h0 * kT + tl] = ss;
       __syncthreads();
       if (!valid) return;
-      r = rnorm[tl];
+      double t = 0.0;
+      for (int g = 0; g < hstep; ++g) t += red[g * kT + tl];
+      r = 1.0 / sqrt(t / (double)((int64_t)H * D) + segs.norm_eps);
     }
     auto store = [&](int h, u32x4 v) {
       const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
@@ -325,7 +330,8 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
 template <bool PERMUTE, bool ROPE, bool NORM = false>
 hipError_t launch_typed(bool bf16, const SegArgs& segs, void* out, int64_t B, int64_t H, int64_t D,
                         const RopeArgs& rope, hipStream_t stream) {
-  const int64_t n_tb = (segs.S + kTok - 1) / kTok;  // token blocks per batch row
+  constexpr int kT = NORM ? kTokNorm : kTok;
+  const int64_t n_tb = (segs.S + kT - 1) / kT;  // token blocks per batch row
   const unsigned grid = (unsigned)(n_tb * B);
   if (bf16)
     rope_permute_kernel<true, PERMUTE, ROPE, NORM><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb,
