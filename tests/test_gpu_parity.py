@@ -164,6 +164,10 @@ def check_prepared(got: torch.Tensor, ref: np.ndarray, dtype, what=""):
     (torch.bfloat16, 64, (2, 2, 3), (16, 24, 24), 2, 5, (12, 7, 9), (1, 2), False, 1.0),
     (torch.bfloat16, 128, (1, 4, 6), (0, 64, 64), 1, 24, (24, 3, 2), (0, 1, 2), True, 1e-3),  # ~eps scale
     (torch.bfloat16, 128, (2, 3, 3), (32, 48, 48), 1, 2, (18, 0, 5), (0, 2), True, 50.0),
+    # more heads than a thread holds in registers: the chunks past them are re-read
+    (torch.bfloat16, 128, (2, 3, 5), (32, 48, 48), 1, 40, (30, 5, 3), (0, 1, 2), True, 1.0),
+    (torch.float32, 128, (2, 2, 4), (32, 48, 48), 2, 16, (16, 3, 6), (0, 2), True, 1.0),
+    (torch.bfloat16, 64, (1, 3, 4), (16, 24, 24), 1, 56, (12, 2, 1), (0, 1, 2), True, 1.0),
 ])
 def test_permute_with_fused_qknorm(gpu, dtype, D, grid, split, B, H, lens, normed, rope, mult):
     say(f"qknorm {dtype} D={D} B={B} H={H} lens={lens} normed={normed} rope={rope} mult={mult}")
