@@ -26,6 +26,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -95,7 +96,7 @@ def cpu_baseline(w, inp, n_rows: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pro-clip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -114,6 +115,7 @@ def main():
 
     w = by_name(args.workload)
     dev = torch.device("cuda", 0)
+    props = torch.cuda.get_device_properties(dev)
     log(f"workload {w.name}: B={w.B} H={w.H} S={w.S} D={w.D} kv_chunk={w.kv_chunk} {w.dtype}")
     t0 = time.perf_counter()
     inp = make_inputs(w)
@@ -193,6 +195,9 @@ def main():
                    "video_grid": list(w.grid), "joint": dict(w.joint), "kv_chunk": w.kv_chunk,
                    "n_chunks": w.n_chunks, "parallelism": "single-gpu"},
         "attn_ms_per_call": round(attn_avg_ms, 4),
+        "attn_ms_median": round(statistics.median(attn_ms), 4),
+        "attn_ms_min": round(min(attn_ms), 4),
+        "device": {"name": props.name, "compute_units": props.multi_processor_count},
         "attn_tflops": round(achieved, 2),
         "pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
         "roofline": roofline,
