@@ -670,6 +670,15 @@ hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, vo
 
 }  // namespace
 
+bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq) {
+  auto fits = [](int64_t blocks, int64_t threads) {
+    return blocks > 0 && blocks <= (int64_t(1) << 31) - 1 && blocks * threads < (int64_t(1) << 32);
+  };
+  const int64_t nbh = B * H;
+  return fits((nbh + 255) / 256, 256) && fits(nbh * kNormSplit, kNormThreads) &&
+         fits(nbh * ((Sq + kBM - 1) / kBM), kThreads);
+}
+
 int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
                         int64_t* split_len) {
   *split_len = Skv;

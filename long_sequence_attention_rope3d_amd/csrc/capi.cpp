@@ -133,7 +133,8 @@ R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, i
   if (!product(n, {B, Nv, H, D}) || n > kMaxElems) return fail(R3D_EINVAL, "rope3d_apply: tensor too large");
   if (x != y && overlap(x, n * es, y, n * es))
     return fail(R3D_EINVAL, "rope3d_apply: x and y overlap without being identical");
-  if (!launch_fits(((Nv + 7) / 8) * B, 256)) return fail(R3D_EINVAL, "rope3d_apply: B*Nv too large for one launch");
+  if (!launch_fits(((Nv + r3d::kPermuteTok - 1) / r3d::kPermuteTok) * B, r3d::kPermuteThreads))
+    return fail(R3D_EINVAL, "rope3d_apply: B*Nv too large for one launch");
   r3d::RopeArgs ra{};
   int st = build_rope(rope, D, Nv, ra);
   if (st != R3D_OK) return st;
@@ -173,8 +174,6 @@ int permute_impl(const void* const* segs, const int64_t* seg_len, int32_t n_segs
   int64_t n_out;
   if (!product(n_out, {B, H, S, D}) || n_out > kMaxElems)
     return fail(R3D_EINVAL, "joint_concat_permute: output too large");
-  if (!launch_fits(((S + 7) / 8) * B, 256))
-    return fail(R3D_EINVAL, "joint_concat_permute: B*S too large for one launch");
   for (int i = 0; i < n_segs; ++i) {
     int64_t ni;
     product(ni, {B, seg_len[i], H, D});
@@ -206,6 +205,9 @@ int permute_impl(const void* const* segs, const int64_t* seg_len, int32_t n_segs
     }
     sa.norm_eps = eps;
   }
+  const int64_t tok = sa.norm ? r3d::kPermuteTokNorm : r3d::kPermuteTok;  // tokens per block
+  if (!launch_fits(((S + tok - 1) / tok) * B, r3d::kPermuteThreads))
+    return fail(R3D_EINVAL, "joint_concat_permute: B*S too large for one launch");
   return hip_status(r3d::launch_permute(sa, out, dtype == R3D_BF16, B, H, D, ra, (hipStream_t)stream),
                     "joint_concat_permute");
 }
@@ -292,7 +294,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd: tensor too large");
   product(bhq, {B, H, Sq});
-  if (dtype == R3D_BF16 ? !launch_fits(B * H * ((Sq + 127) / 128), 256) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
+  if (dtype == R3D_BF16 ? !r3d::attn_bf16_launches_fit(B, H, Sq) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
     return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
   const void* ins[3] = {q, k, v};
   const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
@@ -363,7 +365,7 @@ R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, v
     return fail(R3D_EINVAL, "attn_fwd: tensor too large");
   product(bhq, {B, H, Sq});
   product(nbh, {B, H});
-  if (!launch_fits(B * H * ((Sq + 127) / 128), 256) || !launch_fits(nbh * 64, 256))
+  if (!r3d::attn_bf16_launches_fit(B, H, Sq))
     return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
   const int es = 2;
   const void* ins[3] = {q, k, v};

@@ -11,6 +11,12 @@ namespace r3d {
 constexpr int kMaxSegs = 8;
 constexpr int kMaxPairs = 64;  // D/2 for D = 128
 
+// rope_permute launches: 256-thread blocks of kPermuteTok consecutive tokens,
+// kPermuteTokNorm with the QK-norm (the host's launch-size checks use these).
+constexpr int kPermuteThreads = 256;
+constexpr int kPermuteTok = 8;
+constexpr int kPermuteTokNorm = 4;
+
 // Rotary tables built on the host: per rotated pair p (0 .. D/2-1) its
 // frequency theta^(-2j/d_axis) (double) and its grid axis.
 struct RopeArgs {
@@ -59,6 +65,11 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
 // n_cus compute units, and *split_len: splitting only when the query tiles
 // alone leave the last round of blocks on the CUs mostly empty.
 constexpr int kMaxKeySplit = 8;
+// True when the launches of one bf16 attn_fwd call without a key split (the
+// zeroing and key-norm pre-pass, and the attention grid) each stay within a
+// 1-D grid's 2^31 - 1 blocks and 2^32 work-items.  (A key split is only
+// chosen for grids of fewer than 4 blocks per CU.)
+bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq);
 int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
                         int64_t* split_len);
 

@@ -35,13 +35,13 @@
 namespace r3d {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTok = 8;
+constexpr int kThreads = kPermuteThreads;
+constexpr int kTok = kPermuteTok;
 // With the QK-norm a block takes 4 tokens, so that each thread holds only a
 // few of its token's chunks (kHold) through the norm's reduction: the kernel
 // then fits 6 waves per SIMD instead of 4, and the latency of the
 // load -> reduce -> store sequence is hidden by more blocks in flight.
-constexpr int kTokNorm = 4;
+constexpr int kTokNorm = kPermuteTokNorm;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));

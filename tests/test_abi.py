@@ -89,6 +89,8 @@ def _attn(fn="r3d_attn_fwd", **kw):
     (dict(out=A), -1, "overlaps"),
     (dict(lse=O + 1024), -1, "overlaps"),
     (dict(B=1 << 40, H=1 << 20), -1, "too large"),
+    # small tensors, but 2^19 heads: the key-norm pre-pass grid would pass 2^32 work-items
+    (dict(B=1 << 10, H=1 << 9, Sq=1, Skv=1), -1, "one launch"),
 ])
 @pytest.mark.parametrize("fn", ["r3d_attn_fwd", "r3d_attn_fwd_bshd"])
 def test_attn_fwd_rejects(fn, kw, status, needle):
@@ -172,6 +174,9 @@ def test_permute_qknorm_rejects():
     assert _permn([A, B_], [10, 5], [None, O + 64]) == -1 and "norm weights" in LIB.r3d_last_error().decode()
     # every plain-permute check still applies
     assert _permn([A, None], [10, 5], [W, None]) == -1 and "segment 1" in LIB.r3d_last_error().decode()
+    # 2^26 tokens: the norm's 4-token blocks would pass 2^32 work-items (8-token blocks would not)
+    assert _permn([1 << 40], [1 << 26], [1 << 42], out=1 << 41) == -1
+    assert "one launch" in LIB.r3d_last_error().decode()
 
 
 def test_lse_merge_rejects():
