@@ -105,7 +105,7 @@ def main():
     ap.add_argument("--no-long-video", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this library runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note, not part of this library).", file=sys.stderr)
         sys.exit(2)
 

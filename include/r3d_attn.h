@@ -36,7 +36,7 @@ extern "C" {
 typedef enum {
   R3D_OK = 0,
   R3D_EINVAL = -1,        /* bad argument: NULL/misaligned pointer, size, split, aliasing */
-  R3D_EUNSUPPORTED = -2,  /* valid request that this build has no kernel for (D, dtype) */
+  R3D_EUNSUPPORTED = -2,  /* valid request that this library has no kernel for (D, dtype) */
   R3D_EHIP = -3           /* the HIP runtime reported an error at launch */
 } r3d_status;
 
