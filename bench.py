@@ -37,6 +37,7 @@ MI355X_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 MI355X_HBM_GBPS = 8000.0
 METRIC = "attention TFLOP/s (4·B·H·Sq·Skv·D) + % bf16 MFMA peak; ms/call at 52k tokens"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_traffic.md")
+MFMA_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_mfma_util.md")
 ATTN_SRC = os.path.join(ROOT, "long_sequence_attention_rope3d_amd", "csrc", "attn_fwd_bf16.hip")
 
 
@@ -55,19 +56,42 @@ def kernel_code_sha256(path: str) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
-def _traffic_for_current_kernel():
-    """HBM bytes per attn_fwd launch from the committed rocprofv3 --pmc summary,
-    or None if there is none or the kernel code changed since it was taken."""
+def _profile_values(path: str, keys):
+    """{key: float} read from a committed rocprofv3 summary, or None if the file or
+    a key is missing or the attention kernel's code changed since it was taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
         src_hash = kernel_code_sha256(ATTN_SRC)
     except OSError:
         return None
     m_hash = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+    if not m_hash or m_hash.group(1) != src_hash:
         return None
-    return float(m_bytes.group(1))
+    vals = {}
+    for key in keys:
+        m = re.search(key + r":\s*([0-9.eE+]+)", text)
+        if not m:
+            return None
+        vals[key] = float(m.group(1))
+    return vals
+
+
+def _traffic_for_current_kernel():
+    """HBM bytes per attn_fwd launch from the committed rocprofv3 --pmc summary,
+    or None if there is none or the kernel code changed since it was taken."""
+    vals = _profile_values(TRAFFIC_FILE, ["hbm_bytes_per_launch"])
+    return None if vals is None else vals["hbm_bytes_per_launch"]
+
+
+def _mfma_counters_for_current_kernel():
+    """Matrix-core busy fraction and the clock the attention kernel ran at, from
+    the committed rocprofv3 --pmc summary (SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE), or None if the kernel code changed since."""
+    vals = _profile_values(MFMA_FILE, ["mfma_busy_frac", "sclk_ghz_under_load"])
+    if vals is None:
+        return None
+    vals["source"] = os.path.relpath(MFMA_FILE, ROOT)
+    return vals
 
 
 def cpu_baseline(w, inp, n_rows: int):
@@ -168,7 +192,8 @@ def main():
     traffic_bytes = _traffic_for_current_kernel()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_bytes, "kernel": "attn_fwd (attn_bf16_kernel<128>)"}
+                "traffic": traffic_bytes, "kernel": "attn_fwd (attn_bf16_kernel<128>)",
+                "counters": _mfma_counters_for_current_kernel()}
 
     cpu = None
     if not args.no_cpu_baseline:

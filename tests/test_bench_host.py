@@ -42,3 +42,19 @@ def test_traffic_is_null_when_the_recorded_hash_differs(tmp_path, monkeypatch):
     assert b._traffic_for_current_kernel() == 1.5e9
     src.write_text("int f() { return 2; }\n")
     assert b._traffic_for_current_kernel() is None
+
+
+def test_mfma_counters_follow_the_kernel_hash(tmp_path, monkeypatch):
+    b = _bench()
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }\n")
+    prof = tmp_path / "mfma.md"
+    prof.write_text(f"kernel_code_sha256: {b.kernel_code_sha256(str(src))}\n"
+                    "mfma_busy_frac: 0.628\nsclk_ghz_under_load: 1.869\n")
+    monkeypatch.setattr(b, "ATTN_SRC", str(src))
+    monkeypatch.setattr(b, "MFMA_FILE", str(prof))
+    c = b._mfma_counters_for_current_kernel()
+    assert c["mfma_busy_frac"] == 0.628 and c["sclk_ghz_under_load"] == 1.869
+    src.write_text("int f() { return 2; }\n")
+    assert b._mfma_counters_for_current_kernel() is None
+
