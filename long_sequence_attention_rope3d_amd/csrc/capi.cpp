@@ -206,7 +206,8 @@ int permute_impl(const void* const* segs, const int64_t* seg_len, int32_t n_segs
     sa.norm_eps = eps;
   }
   const int64_t tok = sa.norm ? r3d::kPermuteTokNorm : r3d::kPermuteTok;  // tokens per block
-  if (!launch_fits(((S + tok - 1) / tok) * B, r3d::kPermuteThreads))
+  const int64_t threads = sa.norm ? r3d::kPermuteThreadsNorm : r3d::kPermuteThreads;
+  if (!launch_fits(((S + tok - 1) / tok) * B, threads))
     return fail(R3D_EINVAL, "joint_concat_permute: B*S too large for one launch");
   return hip_status(r3d::launch_permute(sa, out, dtype == R3D_BF16, B, H, D, ra, (hipStream_t)stream),
                     "joint_concat_permute");

@@ -11,10 +11,12 @@ namespace r3d {
 constexpr int kMaxSegs = 8;
 constexpr int kMaxPairs = 64;  // D/2 for D = 128
 
-// rope_permute launches: 256-thread blocks of kPermuteTok consecutive tokens,
-// kPermuteTokNorm with the QK-norm (the host's launch-size checks use these).
-constexpr int kPermuteThreads = 256;
-constexpr int kPermuteTok = 8;
+// rope_permute launches: blocks of kPermuteThreads threads over kPermuteTok
+// consecutive tokens; with the QK-norm, kPermuteThreadsNorm threads over
+// kPermuteTokNorm tokens (the host's launch-size checks use these).
+constexpr int kPermuteThreads = 512;
+constexpr int kPermuteTok = 4;
+constexpr int kPermuteThreadsNorm = 256;
 constexpr int kPermuteTokNorm = 4;
 
 // Rotary tables built on the host: per rotated pair p (0 .. D/2-1) its

@@ -35,12 +35,19 @@
 namespace r3d {
 namespace {
 
+// Copy / rotate: 512-thread blocks of 4 tokens, so that each thread moves
+// only a few chunks (3 for 24 heads of 128 bf16) and many blocks are in
+// flight: measured 15% faster than 256-thread blocks of 8 tokens whose
+// threads walked 12 heads each (a plain 16-byte-per-thread copy of the same
+// bytes peaks at about 6.5 TB/s on the MI355X).
 constexpr int kThreads = kPermuteThreads;
 constexpr int kTok = kPermuteTok;
-// With the QK-norm a block takes 4 tokens, so that each thread holds only a
-// few of its token's chunks (kHold) through the norm's reduction: the kernel
-// then fits 6 waves per SIMD instead of 4, and the latency of the
-// load -> reduce -> store sequence is hidden by more blocks in flight.
+// With the QK-norm a block is 256 threads over 4 tokens, so that each thread
+// holds only a few of its token's chunks (kHold) through the norm's
+// reduction: the kernel then fits 6 waves per SIMD instead of 4, and the
+// latency of the load -> reduce -> store sequence is hidden by more blocks in
+// flight.
+constexpr int kThreadsNorm = kPermuteThreadsNorm;
 constexpr int kTokNorm = kPermuteTokNorm;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -178,54 +185,69 @@ __device__ __forceinline__ double chunk_sumsq(u32x4 v) {
 // NORM (with PERMUTE, D in {64, 128}): segments with a weight vector get the
 // RMS QK-norm before the rotation.
 template <bool BF16, bool PERMUTE, bool ROPE, bool NORM>
-__global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, void* out,
-                                                                int H, int D, int64_t n_tb, RopeArgs rope) {
-  constexpr int kT = NORM ? kTokNorm : kTok;  // tokens per block
+__global__ __launch_bounds__(NORM ? kThreadsNorm : kThreads) void rope_permute_kernel(
+    SegArgs segs, void* out, int H, int D, int64_t n_tb, RopeArgs rope) {
+  constexpr int kT = NORM ? kTokNorm : kTok;           // tokens per block
+  constexpr int kNT = NORM ? kThreadsNorm : kThreads;  // threads per block
   __shared__ double2 cs[kT][kMaxPairs];
-  // Norm partial sums, one per (head group, token): hstep * kT = kThreads / cpr
+  // Norm partial sums, one per (head group, token): hstep * kT = kNT / cpr
   // of them, and cpr >= 8 for the row widths the norm accepts.
-  __shared__ double red[NORM ? kThreads / 8 : 1];
+  __shared__ double red[NORM ? kNT / 8 : 1];
   const int64_t b = (int64_t)blockIdx.x / n_tb;
   const int64_t tok0 = ((int64_t)blockIdx.x - b * n_tb) * kT;
   const int64_t S = segs.S;
   const int npairs = D / 2;
   const int cpr = D * (BF16 ? 2 : 4) / 16;  // 16-byte chunks per row
 
-  if constexpr (ROPE) {
-    // Token n of the video segment sits at (t, h, w), n = (t*gh + h)*gw + w.
-    const int64_t nv = segs.len[0];
-    for (int e = threadIdx.x; e < kT * npairs; e += kThreads) {
-      const int tl = e / npairs, p = e - tl * npairs;
-      const int64_t s = tok0 + tl;
-      double sn = 0.0, c = 1.0;
-      if (s < nv) {
-        const int64_t w = s % rope.grid_w;
-        const int64_t hw = s / rope.grid_w;
-        const int64_t h = hw % rope.grid_h;
-        const int64_t t = hw / rope.grid_h;
-        const int ax = rope.axis[p];
-        sincos((double)(ax == 0 ? t : (ax == 1 ? h : w)) * rope.omega[p], &sn, &c);
-      }
-      cs[tl][p] = make_double2(c, sn);
+  // cos/sin of the block's token angles into LDS, one table entry (token tl,
+  // pair p) per thread.  The angle is formed first -- its frequency and axis
+  // come from the argument block by a per-thread index, i.e. by vector-memory
+  // loads -- and the fp64 sincos and the LDS write only after the thread has
+  // issued its chunk loads, so the sincos latency overlaps them instead of
+  // waiting for them.  The table is read after the next barrier.
+  static_assert(kT * kMaxPairs <= kNT, "one table entry per thread");
+  double angle = 0.0;
+  const int e_tl = threadIdx.x / npairs, e_p = threadIdx.x - e_tl * npairs;
+  const bool has_entry = ROPE && threadIdx.x < kT * npairs;
+  if (has_entry) {
+    // Token n of the video segment sits at (t, h, w), n = (t*gh + h)*gw + w;
+    // other tokens keep angle 0 (cos 1, sin 0).
+    const int64_t s = tok0 + e_tl;
+    if (s < segs.len[0]) {
+      const int64_t w = s % rope.grid_w;
+      const int64_t hw = s / rope.grid_w;
+      const int64_t h = hw % rope.grid_h;
+      const int64_t t = hw / rope.grid_h;
+      const int ax = rope.axis[e_p];
+      angle = (double)(ax == 0 ? t : (ax == 1 ? h : w)) * rope.omega[e_p];
     }
-    __syncthreads();
   }
+  auto build_table = [&]() {
+    if (has_entry) {
+      double sn, c;
+      sincos(angle, &sn, &c);
+      cs[e_tl][e_p] = make_double2(c, sn);
+    }
+  };
 
   const int per_h = kT * cpr;
   // (The host allows NORM only for D in {64, 128}, which always takes this branch.)
-  if (NORM || (per_h <= kThreads && kThreads % per_h == 0)) {
+  if (NORM || (per_h <= kNT && kNT % per_h == 0)) {
     // Each thread keeps one (token, chunk) slot and walks the heads.
     const int slot = threadIdx.x % per_h;
     const int tl = slot / cpr, chunk = slot - tl * cpr;
-    const int hstep = kThreads / per_h;
+    const int hstep = kNT / per_h;
     const int64_t s = tok0 + tl;
-    const bool valid = s < S;
-    if (!NORM && !valid) return;  // with NORM every thread reaches the barriers below
+    const bool valid = s < S;  // every thread reaches the barrier below
+    // A slot past the last token (last block only) loads token S-1 instead,
+    // in bounds, so that every thread issues the same loads without a branch;
+    // it stores nothing.
+    const int64_t sc = valid ? s : S - 1;
     int seg = 0;
     if constexpr (PERMUTE) {
-      while (valid && seg + 1 < segs.n && s >= segs.off[seg + 1]) ++seg;
+      while (seg + 1 < segs.n && sc >= segs.off[seg + 1]) ++seg;
     }
-    const int64_t ls = s - segs.off[seg];
+    const int64_t ls = sc - segs.off[seg];
     const u32x4* src = reinterpret_cast<const u32x4*>(segs.src[seg]) + ((b * segs.len[seg] + ls) * H) * cpr + chunk;
     u32x4* dst = reinterpret_cast<u32x4*>(out);
     const bool rot = ROPE && seg == 0;
@@ -233,13 +255,23 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
     const float* wn = nullptr;
     double r = 1.0;
     const int h0 = threadIdx.x / per_h;
-    // With a norm, the thread's first kHold chunks (heads h0, h0 + hstep, ...)
-    // are loaded once, all in flight together, summed, and kept in registers
-    // for the normalise / rotate / store pass; heads beyond them (only for
-    // H > kHold * hstep) are read again from L2.
-    constexpr int kHold = NORM ? 6 : 1;  // all of them for bf16, D = 128, H <= 24
+    // The thread's first kHold chunks (heads h0, h0 + hstep, ...) are loaded
+    // first, all in flight together, and kept in registers for the
+    // normalise / rotate / store pass (with a norm they are also summed);
+    // heads beyond them (only for H > kHold * hstep) are read afterwards.
+    // The loads take no branch (a slot past the thread's last head re-reads
+    // head H-1 of the same token, in bounds, and is not used): with a branch
+    // around them the compiler copied the loaded registers at the join, i.e.
+    // waited for the loads before the table below.
+    constexpr int kHold = NORM ? 6 : 3;  // all of them for bf16, D = 128, H <= 24
     u32x4 held[kHold];
     const int nh = (valid && H > h0) ? (H - h0 + hstep - 1) / hstep : 0;  // this thread's heads
+    auto ld = [&](int h) {
+      return NORM ? src[(int64_t)h * cpr] : __builtin_nontemporal_load(src + (int64_t)h * cpr);
+    };
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) held[i] = ld(min(h0 + i * hstep, H - 1));
+    build_table();
     if constexpr (NORM) {
       // Pass 1: the token's sum of squares over all H*D values.  The cpr
       // threads of token tl in each of the hstep head groups are consecutive
@@ -251,19 +283,20 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
       if (wn) {
 #pragma unroll
         for (int i = 0; i < kHold; ++i)
-          if (i < nh) held[i] = src[(int64_t)(h0 + i * hstep) * cpr];
-#pragma unroll
-        for (int i = 0; i < kHold; ++i)
           if (i < nh) ss += chunk_sumsq<BF16>(held[i]);
         for (int h = h0 + kHold * hstep; h < H; h += hstep) ss += chunk_sumsq<BF16>(src[(int64_t)h * cpr]);
       }
       for (int m = cpr / 2; m > 0; m >>= 1) ss += __shfl_xor(ss, m, cpr);
       if (chunk == 0) red[h0 * kT + tl] = ss;
-      __syncthreads();
+      __syncthreads();  // also publishes the cos/sin table
       if (!valid) return;
       double t = 0.0;
       for (int g = 0; g < hstep; ++g) t += red[g * kT + tl];
       r = 1.0 / sqrt(t / (double)((int64_t)H * D) + segs.norm_eps);
+    }
+    if constexpr (!NORM) {
+      if constexpr (ROPE) __syncthreads();  // the cos/sin table
+      if (!valid) return;
     }
     auto store = [&](int h, u32x4 v) {
       const int64_t o = PERMUTE ? (((b * H + h) * S + s) * cpr + chunk) : (((b * S + s) * H + h) * cpr + chunk);
@@ -297,18 +330,27 @@ __global__ __launch_bounds__(kThreads) void rope_permute_kernel(SegArgs segs, vo
         store(h, norm_rotate_chunk<BF16>(src[(int64_t)h * cpr], r, wa, wb, rot ? cs[tl] : nullptr, chunk));
       }
     } else {
-      // Copy / rotate (the only pass without a norm).
-#pragma unroll 4
-      for (int h = h0; h < H; h += hstep) {
-        u32x4 v = __builtin_nontemporal_load(src + (int64_t)h * cpr);
+      // Copy / rotate: the held chunks, then any remaining heads.
+#pragma unroll
+      for (int i = 0; i < kHold; ++i) {
+        if (i < nh) {
+          u32x4 v = held[i];
+          if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
+          store(h0 + i * hstep, v);
+        }
+      }
+      for (int h = h0 + kHold * hstep; h < H; h += hstep) {
+        u32x4 v = ld(h);
         if (rot) v = rotate_chunk<BF16>(v, cs[tl], chunk);
         store(h, v);
       }
     }
   } else {
     // Generic row widths (no RoPE: any D whose row is a multiple of 16 bytes).
+    build_table();
+    if constexpr (ROPE) __syncthreads();
     const int64_t items = (int64_t)per_h * H;
-    for (int64_t idx = threadIdx.x; idx < items; idx += kThreads) {
+    for (int64_t idx = threadIdx.x; idx < items; idx += kNT) {
       const int h = (int)(idx / per_h);
       const int slot = (int)(idx - (int64_t)h * per_h);
       const int tl = slot / cpr, chunk = slot - tl * cpr;
@@ -331,14 +373,13 @@ template <bool PERMUTE, bool ROPE, bool NORM = false>
 hipError_t launch_typed(bool bf16, const SegArgs& segs, void* out, int64_t B, int64_t H, int64_t D,
                         const RopeArgs& rope, hipStream_t stream) {
   constexpr int kT = NORM ? kTokNorm : kTok;
+  constexpr int kNT = NORM ? kThreadsNorm : kThreads;
   const int64_t n_tb = (segs.S + kT - 1) / kT;  // token blocks per batch row
   const unsigned grid = (unsigned)(n_tb * B);
   if (bf16)
-    rope_permute_kernel<true, PERMUTE, ROPE, NORM><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb,
-                                                                                  rope);
+    rope_permute_kernel<true, PERMUTE, ROPE, NORM><<<grid, kNT, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
   else
-    rope_permute_kernel<false, PERMUTE, ROPE, NORM><<<grid, kThreads, 0, stream>>>(segs, out, (int)H, (int)D, n_tb,
-                                                                                   rope);
+    rope_permute_kernel<false, PERMUTE, ROPE, NORM><<<grid, kNT, 0, stream>>>(segs, out, (int)H, (int)D, n_tb, rope);
   return hipGetLastError();
 }
 
