@@ -168,7 +168,8 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  * on that stream first, so that the captured call needs no allocation (a
  * growth inside capture fails with R3D_EHIP).
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
- * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype), R3D_EHIP.
+ * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype, or for R3D_BF16 an
+ * Sq or Skv above 2^31 - 1024: that kernel indexes rows in 32 bits), R3D_EHIP.
  */
 R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                          int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,

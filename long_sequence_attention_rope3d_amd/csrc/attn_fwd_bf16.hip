@@ -104,11 +104,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per block
 constexpr int kWavesPerSimd = kWaves / 4;  // waves per SIMD (one block per CU)
 static_assert(kWaves % 4 == 0, "whole waves per SIMD");
+static_assert(kAttnMaxSeq + kBM <= INT32_MAX, "query rows fit in 32 bits");
 static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 #ifndef R3D_ATTN_BN
 #define R3D_ATTN_BN 128
 #endif
 constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
+static_assert(kAttnMaxSeq + kBN <= INT32_MAX, "key cursor fits in 32 bits");
 constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
 constexpr float kTau = 0.0f;      // rescale threshold, log2 units (0: on every new maximum)
@@ -187,15 +189,19 @@ __device__ __forceinline__ int key_of_row(int m) { return (m & ~12) | ((m & 4) <
 
 // Walks the key tiles in order: tiles of kBN keys inside chunks of `chunk`
 // keys (the last tile of a chunk may be short), advanced by additions only.
+// Key indices are 32-bit (the host keeps Sq and Skv within kAttnMaxSeq): the
+// tile bookkeeping then stays on the scalar unit, where 64-bit compares
+// would each cost vector instructions (gfx9 has no scalar 64-bit less-than),
+// and the cursor never overflows (every sum below is bounded by Skv + kBN).
 struct TileCursor {
-  int64_t kv0;   // first key of the tile
-  int64_t cend;  // end of the tile's chunk
-  __device__ __forceinline__ int n() const { return (int)((kv0 + kBN < cend) ? kBN : cend - kv0); }
-  __device__ __forceinline__ void advance(int64_t chunk, int64_t Skv) {
+  int kv0;   // first key of the tile
+  int cend;  // end of the tile's chunk
+  __device__ __forceinline__ int n() const { return (cend - kv0 > kBN) ? kBN : cend - kv0; }
+  __device__ __forceinline__ void advance(int chunk, int Skv) {
     kv0 += kBN;
     if (kv0 >= cend) {
       kv0 = cend;
-      cend = (cend + chunk < Skv) ? cend + chunk : Skv;
+      cend = (Skv - cend > chunk) ? cend + chunk : Skv;
     }
   }
 };
@@ -311,13 +317,16 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   const int split = hs - (int)bh * n_split;
   // This block's keys: [kv_begin, kv_end), a whole number of chunks (or, with
   // one chunk, of tiles); n_split = 1 is the whole sequence.
-  const int64_t kv_begin = (int64_t)split * split_len;
-  const int64_t kv_end = kv_begin + split_len < Skv ? kv_begin + split_len : Skv;
+  const int skv = (int)Skv;
+  const int chunk32 = (int)(chunk < Skv ? chunk : Skv);
+  const int kv_begin = split * (int)split_len;
+  const int kv_end = (skv - kv_begin > (int)split_len) ? kv_begin + (int)split_len : skv;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31, hf = lane >> 5;
-  const int64_t qrow = (int64_t)qt * kBM + wave * 32 + r32;
+  const int qrow = qt * kBM + wave * 32 + r32;  // < Sq + kBM <= 2^31
+  const int sq = (int)Sq;
   const uint16_t* kb = k + bh * Skv * D;
   const uint16_t* vb = v + bh * Skv * D;
 
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < G::kSteps; ++s) {
     u32x4 x = u32x4{0, 0, 0, 0};
-    if (qrow < Sq) x = *reinterpret_cast<const u32x4*>(q + (bh * Sq + qrow) * D + 16 * s + 8 * hf) ^ qsign;
+    if (qrow < sq) x = *reinterpret_cast<const u32x4*>(q + (bh * Sq + qrow) * D + 16 * s + 8 * hf) ^ qsign;
     qf[s] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   bool need_max = true;
   auto update_need_max = [&]() { need_max = __ballot(bnd > m_run + kSlack) != 0; };
 
-  const int64_t first_cend = kv_begin + chunk < kv_end ? kv_begin + chunk : kv_end;
+  const int first_cend = (kv_end - kv_begin > chunk32) ? kv_begin + chunk32 : kv_end;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
   TileCursor pf{kv_begin, first_cend};
   // Copy tile pf into stage P (K and V), then advance pf.
@@ -390,8 +399,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const int n = pf.n();
     const uint32_t lk = lds_u32(P == 0 ? st0_k : P == 1 ? st1_k : st2_k);
     const uint32_t lv = lds_u32(P == 0 ? st0_v : P == 1 ? st1_v : st2_v);
-    const uint16_t* ks = kb + pf.kv0 * D;
-    const uint16_t* vs = vb + pf.kv0 * D;
+    const uint16_t* ks = kb + (int64_t)pf.kv0 * D;
+    const uint16_t* vs = vb + (int64_t)pf.kv0 * D;
     if (n == kBN) {
       dma_tile<D, false, true>(lk, ks, n, wave, lane);
       dma_tile<D, true, true>(lv, vs, n, wave, lane);
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       dma_tile<D, false, false>(lk, ks, n, wave, lane);
       dma_tile<D, true, false>(lv, vs, n, wave, lane);
     }
-    pf.advance(chunk, kv_end);
+    pf.advance(chunk32, kv_end);
   };
   copy(std::integral_constant<int, 0>{});
   if (kStages == 3 && pf.kv0 < kv_end) copy(std::integral_constant<int, 1>{});
@@ -466,8 +475,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       // The row max is compared in raw logit units against thr, so the
       // common step (no row moves) spends one compare; only a step in which
       // some row's max exceeds its threshold forms the new reference.
-      float m_use = m_run;
+      // A moved reference takes effect at once (m_run is updated here, the
+      // factor alpha for acc and l kept for the rescale below), so the common
+      // step reads m_run itself and needs no copy of it.
       bool moved = false;  // wave-uniform
+      float alpha;  // set (and read) only when the reference moved
       if (!kConstMax && need_max) {
         float mx = sacc[0];
 #pragma unroll
@@ -475,12 +487,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         mx = max_halves(mx);
         const bool up = mx > thr;
         if (__builtin_expect(__ballot(up) != 0, 0)) {
-          m_use = up ? mx * c : m_run;
+          const float m_new = up ? mx * c : m_run;
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where the row kept it, 0 from m = -inf
+          m_run = m_new;
           moved = true;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_use));
+      for (int i = 0; i < 16; ++i) sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -m_run));
       // Row sum from the unrounded fp32 p (keeps lse at fp32 accuracy).
       float ps = sacc[0];
 #pragma unroll
@@ -504,11 +518,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       // a chunk's first step): acc already holds step h2-1's PV (issued above),
       // and step h2's PV comes after.
       if (!kConstMax && moved) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);  // 1 where the row kept it
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
-        m_run = m_use;
         thr = (m_run + kTau) * inv_c;
         update_need_max();
       }
@@ -535,7 +547,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       update_need_max();
       l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
     }
-    cur.advance(chunk, kv_end);
+    cur.advance(chunk32, kv_end);
   };
 
   // Tiles run through the stages in a straight line; a chunk's last tile ends
@@ -563,22 +575,29 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   // ---- epilogue: out (bf16, RNE; or fp32 for a key-split partial) and lse (natural log) ----
   // The last tile closed a chunk, so acc = O and m = L (log2).
   // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
-  if (qrow < Sq) {
+  // The lane's row and half are formed again here from the hardware lane
+  // count (v_mbcnt), which the compiler cannot identify with the thread-id
+  // arithmetic above: no per-lane value of the prologue (or 64-bit form of
+  // one) stays live across the key loop, where every register is taken.
+  const int e_lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int e_hf = e_lane >> 5;
+  const int e_qrow = qt * kBM + wave * 32 + (e_lane & 31);
+  if (e_qrow < sq) {
     // Row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major); a
     // split partial goes to [n_split, B*H*Sq, D] (lse [n_split, B*H*Sq]).
     const int64_t b = bh / H;
     const int64_t nbh = (int64_t)n_blocks / ((int64_t)n_split * n_qt);  // B*H
-    const int64_t prow = ((int64_t)split * nbh + bh) * Sq + qrow;
+    const int64_t prow = ((int64_t)split * nbh + bh) * Sq + e_qrow;
     if (out_f32) {
       float* op = static_cast<float*>(out) + prow * D;
 #pragma unroll
       for (int b = 0; b < G::kDBlk; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(op + 32 * b + 8 * g + 4 * hf) =
+          *reinterpret_cast<float4*>(op + 32 * b + 8 * g + 4 * e_hf) =
               make_float4(oacc[b][4 * g], oacc[b][4 * g + 1], oacc[b][4 * g + 2], oacc[b][4 * g + 3]);
     } else {
-      const int64_t orow = out_bshd ? (b * Sq + qrow) * H + (bh - b * H) : prow;
+      const int64_t orow = out_bshd ? (b * Sq + e_qrow) * H + (bh - b * H) : prow;
       uint16_t* op = static_cast<uint16_t*>(out) + orow * D;
 #pragma unroll
       for (int b = 0; b < G::kDBlk; ++b)
@@ -586,10 +605,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         for (int g = 0; g < 4; ++g) {
           const u32x2 w = u32x2{pack_bf16(oacc[b][4 * g], oacc[b][4 * g + 1]),
                                 pack_bf16(oacc[b][4 * g + 2], oacc[b][4 * g + 3])};
-          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * hf) = w;
+          *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * e_hf) = w;
         }
     }
-    if (lse && hf == 0) lse[prow] = m_run * 0.69314718055994530942f;
+    if (lse && e_hf == 0) lse[prow] = m_run * 0.69314718055994530942f;
   }
 }
 

@@ -291,6 +291,9 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   if (kv_chunk < 0) return fail(R3D_EINVAL, "attn_fwd: kv_chunk=%lld < 0", (long long)kv_chunk);
   if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
   if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
+  if (dtype == R3D_BF16 && (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq))
+    return fail(R3D_EUNSUPPORTED, "attn_fwd: Sq=%lld, Skv=%lld (bf16: at most %lld each)", (long long)Sq,
+                (long long)Skv, (long long)r3d::kAttnMaxSeq);
   int64_t nq, nk, bhq;
   if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd: tensor too large");
@@ -361,6 +364,9 @@ R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, v
     return fail(R3D_EINVAL, "attn_fwd: B, H, Sq, Skv, D must be > 0");
   if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
   if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
+  if (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq)
+    return fail(R3D_EUNSUPPORTED, "attn_fwd: Sq=%lld, Skv=%lld (bf16: at most %lld each)", (long long)Sq,
+                (long long)Skv, (long long)r3d::kAttnMaxSeq);
   int64_t nq, nk, bhq, nbh;
   if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd: tensor too large");

@@ -9,6 +9,11 @@
 namespace r3d {
 
 constexpr int kMaxSegs = 8;
+
+// Largest Sq and Skv of a bf16 attention call: the kernel keeps query and key
+// indices in 32 bits, with a margin for one query tile and one key tile past
+// the end.
+constexpr int64_t kAttnMaxSeq = (int64_t(1) << 31) - 1024;
 constexpr int kMaxPairs = 64;  // D/2 for D = 128
 
 // rope_permute launches: blocks of kPermuteThreads threads over kPermuteTok

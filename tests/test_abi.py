@@ -91,6 +91,9 @@ def _attn(fn="r3d_attn_fwd", **kw):
     (dict(B=1 << 40, H=1 << 20), -1, "too large"),
     # small tensors, but 2^19 heads: the key-norm pre-pass grid would pass 2^32 work-items
     (dict(B=1 << 10, H=1 << 9, Sq=1, Skv=1), -1, "one launch"),
+    # bf16 rows are indexed in 32 bits: at most 2^31 - 1024 query or key rows
+    (dict(H=1, Sq=(1 << 31) - 1023, D=64), -2, "at most 2147482624"),
+    (dict(H=1, Skv=(1 << 31) - 1023, D=64), -2, "at most 2147482624"),
 ])
 @pytest.mark.parametrize("fn", ["r3d_attn_fwd", "r3d_attn_fwd_bshd"])
 def test_attn_fwd_rejects(fn, kw, status, needle):
@@ -100,14 +103,16 @@ def test_attn_fwd_rejects(fn, kw, status, needle):
 
 def test_attn_fwd_constmax_rejects():
     W = 0x70000000
-    def call(ws=W, dtype=1, D=128, out=O):
-        return LIB.r3d_attn_fwd_constmax(A, B_, C, out, L_, ws, 1, 2, 64, 64, D, 0.125, dtype, None)
+    def call(ws=W, dtype=1, D=128, out=O, Sq=64, Skv=64):
+        return LIB.r3d_attn_fwd_constmax(A, B_, C, out, L_, ws, 1, 2, Sq, Skv, D, 0.125, dtype, None)
     assert call(dtype=0) == -2 and "bf16" in LIB.r3d_last_error().decode()
     assert call(ws=None) == -1 and "workspace" in LIB.r3d_last_error().decode()
     assert call(ws=W + 2) == -1
     assert call(ws=O + 64) == -1 and "overlaps" in LIB.r3d_last_error().decode()
     assert call(D=96) == -2
     assert call(out=A) == -1
+    assert call(Sq=(1 << 31) - 1023, D=64) == -2 and "at most" in LIB.r3d_last_error().decode()
+    assert call(Skv=(1 << 31) - 1023, D=64) == -2
 
 
 class Rope(ctypes.Structure):
