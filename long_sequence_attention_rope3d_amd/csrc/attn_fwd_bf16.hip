@@ -300,9 +300,14 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     int n_split, int64_t split_len, int out_f32) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
-  __shared__ __attribute__((aligned(1024))) uint16_t st0_k[G::kTile], st0_v[G::kTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t st1_k[G::kTile], st1_v[G::kTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t st2_k[G::kTile], st2_v[G::kTile];
+  // K/V stage buffers in one array, K stages first: [K_0 .. K_{kStages-1} | V_0 .. V_{kStages-1}].
+  // A DS instruction's immediate offset has 16 bits, so every operand read
+  // must reach its byte with a constant below 64 KB: K reads add at most
+  // (kStages-1) tiles + 3 steps to their lane offset, and V reads carry the V
+  // region's start inside their per-lane base registers (see v_base), so
+  // neither needs an address instruction per read.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * G::kTile];
+  static_assert((kStages - 1) * G::kTile * 2 + kBN * G::kCpr * 16 <= 65536, "K reads within the DS offset");
 
   // Block -> (head, key split, query tile): XCD x runs logical tiles
   // [x*per + min(x, rem), ...), and consecutive logical tiles are consecutive
@@ -359,7 +364,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const int d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int b = 0; b < G::kDBlk; ++b)
-      v_base[b] = (row * G::kCpr + (((32 * b + d) >> 3) ^ swz_v<D>(row))) * 16 + (d & 7) * 2;
+    {
+      int vb = kStages * G::kTile * 2 + (row * G::kCpr + (((32 * b + d) >> 3) ^ swz_v<D>(row))) * 16 + (d & 7) * 2;
+      asm volatile("" : "+v"(vb));  // keep the V region's start in the register, out of the offsets
+      v_base[b] = vb;
+    }
   }
 
   f32x16 oacc[G::kDBlk];
@@ -397,8 +406,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   auto copy = [&](auto stage) {
     constexpr int P = decltype(stage)::value;
     const int n = pf.n();
-    const uint32_t lk = lds_u32(P == 0 ? st0_k : P == 1 ? st1_k : st2_k);
-    const uint32_t lv = lds_u32(P == 0 ? st0_v : P == 1 ? st1_v : st2_v);
+    const uint32_t lk = lds_u32(lds + P * G::kTile);
+    const uint32_t lv = lds_u32(lds + (kStages + P) * G::kTile);
     const uint16_t* ks = kb + (int64_t)pf.kv0 * D;
     const uint16_t* vs = vb + (int64_t)pf.kv0 * D;
     if (n == kBN) {
@@ -427,8 +436,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const bool issue = pf.kv0 < kv_end;
     if (issue) copy(std::integral_constant<int, (S + kStages - 1) % kStages>{});  // the tile kStages-1 ahead
 
-    const char* kt = reinterpret_cast<const char*>(S == 0 ? st0_k : S == 1 ? st1_k : st2_k);
-    char* vt = reinterpret_cast<char*>(S == 0 ? st0_v : S == 1 ? st1_v : st2_v);
+    const char* kt = reinterpret_cast<const char*>(lds + S * G::kTile);
+    char* vt = reinterpret_cast<char*>(lds) + S * G::kTile * 2;  // v_base holds the V region's start
     // 32-key steps, software-pipelined inside the tile: step h's S^T = K Q^T
     // is issued before step h-1's PV product, so the matrix core runs that PV
     // while the same wave computes step h's softmax on the VALU.  In a short
