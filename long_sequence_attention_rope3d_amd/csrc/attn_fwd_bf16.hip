@@ -73,9 +73,9 @@
 //   first step, and later steps spend no VALU work on the max at all.
 // * The row sum l adds the fp32 p before their bf16 rounding for the PV
 //   product, so lse keeps fp32 accuracy.
-// * Issue priority: with the online max, a wave raises its priority
-//   (s_setprio) while it issues a step's MFMAs and drops it for its softmax,
-//   so the SIMD's arbiter serves the matrix core first.
+// * Issue priority: every wave keeps the default priority.  Raising it
+//   while a wave issues its MFMAs once paid 1%, but with the VALU trimmed as
+//   it is now it costs 0.5% (52k and long-video alike).
 #include <type_traits>
 
 #include "launch.h"
@@ -448,13 +448,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 #pragma unroll
     for (int h2 = 0; h2 <= kSub; ++h2) {
       f32x16 sacc = f32x16{};
-      // While a wave issues its matrix instructions it outranks the SIMD's
-      // other waves (which are then in their softmax), so the matrix core
-      // is fed first and the VALU work fills the gaps; the priority drops
-      // again before this wave's own softmax.  (Measured: 1-1.4% faster with
-      // the online max, 1.4% slower in the constant-max form, which keeps
-      // the default arbitration.)
-      if constexpr (!kConstMax) __builtin_amdgcn_s_setprio(1);
       if (h2 < kSub) {
         // ---- S^T = K Q^T for keys [32*h2, 32*h2 + 32) ----
 #pragma unroll
@@ -477,7 +470,6 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
           }
         }
       }
-      if constexpr (!kConstMax) __builtin_amdgcn_s_setprio(0);
       if (h2 == kSub) break;
 
       // ---- online softmax, log2 domain; element i is key 32*h2 + 16*(i/8) + 8*hf + i%8 ----
