@@ -31,7 +31,7 @@
 // * Block = 12 waves = 384 query rows (32 per wave), one block per CU, i.e.
 //   three waves per SIMD: while one wave of a SIMD runs its softmax on the
 //   VALU or waits on LDS, the others keep the matrix core busy.  That caps a
-//   wave at 168 registers (the kernel needs ~166 and spills nothing).  384
+//   wave at 168 registers (the kernel needs 162 and spills nothing).  384
 //   also divides the 52608-token workload exactly, and 137 query tiles per
 //   head keep the last round of blocks on the CUs nearly full.
 // * Grid = B*H*n_split*ceil(Sq/384) blocks, re-numbered so consecutive query
