@@ -133,7 +133,7 @@ R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, i
   if (!product(n, {B, Nv, H, D}) || n > kMaxElems) return fail(R3D_EINVAL, "rope3d_apply: tensor too large");
   if (x != y && overlap(x, n * es, y, n * es))
     return fail(R3D_EINVAL, "rope3d_apply: x and y overlap without being identical");
-  if (!launch_fits(((Nv + r3d::kPermuteTok - 1) / r3d::kPermuteTok) * B, r3d::kPermuteThreads))
+  if (!launch_fits(((Nv + r3d::kPermuteTokRope - 1) / r3d::kPermuteTokRope) * B, r3d::kPermuteThreadsRope))
     return fail(R3D_EINVAL, "rope3d_apply: B*Nv too large for one launch");
   r3d::RopeArgs ra{};
   int st = build_rope(rope, D, Nv, ra);
@@ -205,8 +205,10 @@ int permute_impl(const void* const* segs, const int64_t* seg_len, int32_t n_segs
     }
     sa.norm_eps = eps;
   }
-  const int64_t tok = sa.norm ? r3d::kPermuteTokNorm : r3d::kPermuteTok;  // tokens per block
-  const int64_t threads = sa.norm ? r3d::kPermuteThreadsNorm : r3d::kPermuteThreads;
+  // tokens and threads per block of the path launch_permute takes
+  const bool rot = rope_seg0 != nullptr;
+  const int64_t tok = sa.norm ? r3d::kPermuteTokNorm : rot ? r3d::kPermuteTokRope : r3d::kPermuteTok;
+  const int64_t threads = sa.norm ? r3d::kPermuteThreadsNorm : rot ? r3d::kPermuteThreadsRope : r3d::kPermuteThreads;
   if (!launch_fits(((S + tok - 1) / tok) * B, threads))
     return fail(R3D_EINVAL, "joint_concat_permute: B*S too large for one launch");
   return hip_status(r3d::launch_permute(sa, out, dtype == R3D_BF16, B, H, D, ra, (hipStream_t)stream),

@@ -16,11 +16,14 @@ constexpr int kMaxSegs = 8;
 constexpr int64_t kAttnMaxSeq = (int64_t(1) << 31) - 1024;
 constexpr int kMaxPairs = 64;  // D/2 for D = 128
 
-// rope_permute launches: blocks of kPermuteThreads threads over kPermuteTok
-// consecutive tokens; with the QK-norm, kPermuteThreadsNorm threads over
-// kPermuteTokNorm tokens (the host's launch-size checks use these).
+// rope_permute launches, per path (the host's launch-size checks use these):
+// plain copy, blocks of kPermuteThreads threads over kPermuteTok consecutive
+// tokens; with RoPE, kPermuteThreadsRope over kPermuteTokRope; with the
+// QK-norm, kPermuteThreadsNorm over kPermuteTokNorm.
 constexpr int kPermuteThreads = 512;
 constexpr int kPermuteTok = 4;
+constexpr int kPermuteThreadsRope = 256;
+constexpr int kPermuteTokRope = 2;
 constexpr int kPermuteThreadsNorm = 256;
 constexpr int kPermuteTokNorm = 4;
 
