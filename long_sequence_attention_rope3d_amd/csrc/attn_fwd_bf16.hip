@@ -482,12 +482,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       bool moved = false;  // wave-uniform
       float alpha;  // set (and read) only when the reference moved
       if (!kConstMax && need_max) {
+        // This lane's 16 keys first: a half-row above the threshold means its
+        // row is above it too, so the cross-half maximum is only formed in
+        // the rare step in which some row moves.
         float mx = sacc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = vmax(mx, sacc[i]);
-        mx = max_halves(mx);
-        const bool up = mx > thr;
-        if (__builtin_expect(__ballot(up) != 0, 0)) {
+        if (__builtin_expect(__ballot(mx > thr) != 0, 0)) {
+          mx = max_halves(mx);
+          const bool up = mx > thr;
           const float m_new = up ? mx * c : m_run;
           alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where the row kept it, 0 from m = -inf
           m_run = m_new;
