@@ -125,9 +125,15 @@ def test_rope3d_apply(gpu, dtype, D, grid, split, B, H):
     check_rope(xd, x, grid, split, "in-place")
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
-def test_permute_with_fused_rope(gpu, dtype, D):
-    grid, split = ((3, 6, 7), (32, 48, 48)) if D == 128 else ((2, 8, 15), (16, 24, 24))
+@pytest.mark.parametrize("dtype,D,grid", [
+    (torch.bfloat16, 128, (3, 6, 7)),
+    (torch.float32, 64, (2, 8, 15)),
+    # odd video length and odd total (105 + 19 + 5 = 129): a block of the RoPE
+    # path straddles the video/audio boundary, and the last one has an idle slot
+    (torch.bfloat16, 128, (3, 5, 7)),
+])
+def test_permute_with_fused_rope(gpu, dtype, D, grid):
+    split = (32, 48, 48) if D == 128 else (16, 24, 24)
     Nv = grid[0] * grid[1] * grid[2]
     B, H = 2, 3
     segs = [_rand((B, Nv, H, D), dtype, 31), _rand((B, 19, H, D), dtype, 32),
