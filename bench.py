@@ -150,6 +150,8 @@ def main():
     q = torch.empty((w.B, w.H, w.S, w.D), dtype=tdt, device=dev)
     k, v, out = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, r3d.attn_fwd_workspace_size(w.B, w.H, w.S, w.S, w.D, w.kv_chunk, tdt)),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -158,7 +160,7 @@ def main():
         r3d.joint_concat_permute(segs["v"], None, out=v)
         if ev is not None:
             ev[0].record(stream)
-        r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk, out=out, lse=lse)
+        r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk, out=out, lse=lse, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -294,7 +296,8 @@ def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps
     log(f"attn_fwd_bshd: {ms:.3f} ms, {res['attn_fwd_bshd']['TFLOPs']:.1f} TFLOP/s")
     # the constant-max variant (Cauchy-Schwarz row bound; key-norm pre-pass included)
     if w.dtype == "bf16":
-        ws = torch.empty(w.B * w.H, dtype=torch.float32, device=dev)
+        ws = torch.empty(r3d.attn_fwd_constmax_workspace_size(w.B, w.H, w.S, w.S, w.D, q.dtype),
+                         dtype=torch.uint8, device=dev)
         ms = timed(lambda: r3d.attn_fwd_constmax(q, k, v, scale=w.scale, out=obshd.view(q.shape), lse=lse,
                                                  workspace=ws))
         res["attn_fwd_constmax"] = {"ms": round(ms, 4),

@@ -8,6 +8,11 @@
  *  - Buffers are DEVICE pointers owned by the caller, contiguous (row-major)
  *    in the layout stated per call, 16-byte aligned.  The library allocates
  *    nothing, keeps no pointer after it returns, and creates no stream.
+ *    Calls that need device scratch memory take a caller-owned `workspace`
+ *    of at least the size their *_workspace_size query reports; its contents
+ *    on entry and on return mean nothing to the caller, and it is used in
+ *    stream order on `stream` (do not hand it to other work until the call's
+ *    work on that stream has finished).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    null stream).  A return of R3D_OK means the work was enqueued; errors of
  *    the kernels themselves surface on the stream like any HIP error.
@@ -21,6 +26,7 @@
 #ifndef R3D_ATTN_H
 #define R3D_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -150,6 +156,12 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  *   D   : 64 or 128.  dtype R3D_BF16 runs on bf16 MFMA with fp32 accumulation and an
  *         fp32 softmax (P rounded to bf16 for the PV product); R3D_F32 is an all-fp32
  *         path.
+ *   workspace, workspace_bytes : device scratch of at least
+ *         r3d_attn_fwd_workspace_size(...) bytes (0 for R3D_F32, where workspace may be
+ *         NULL), 16-byte aligned, overlapping no tensor of the call.  The R3D_BF16 path
+ *         keeps there per-head statistics of K and V (2*B*H*64 floats: partial maxima of
+ *         |k_j|^2 for a Cauchy-Schwarz bound on every row's logits, and of |v|) and, for
+ *         a key-split launch, the fp32 partials (below).
  * Key split: an R3D_BF16 launch whose query tiles leave the GPU's compute
  *   units mostly idle (fewer tiles than an eighth of them, or a last round of
  *   tiles at most a quarter full) splits every tile's keys into up to 8 ranges
@@ -157,27 +169,31 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  *   its own block, and merges the fp32 partials (O, lse) with the lse_merge
  *   kernel -- the ring's per-shard partial + merge, on one device.  The result
  *   equals the unsplit one up to rounding.  r3d_attn_fwd_bshd never splits.
- * Memory: the R3D_BF16 path keeps library-owned device workspaces, one per
- * (current device, stream, kind): B*H floats (each head's largest squared key
- * norm, from which every row gets a Cauchy-Schwarz bound on its logits) and,
- * for split launches, n_split*B*H*Sq*(D+1) floats of partials.  The first call
- * on a stream that needs one, or a call that needs more than any before on it,
- * allocates it with hipMalloc (after synchronizing that stream when it grows);
- * later calls allocate nothing.  Calls on one stream reuse them in stream order.
- * Under HIP graph capture make one uncaptured call of the same or larger sizes
- * on that stream first, so that the captured call needs no allocation (a
- * growth inside capture fails with R3D_EHIP).
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
- * out/lse overlapping an input), R3D_EUNSUPPORTED (D, dtype, or for R3D_BF16 an
- * Sq or Skv above 2^31 - 1024: that kernel indexes rows in 32 bits), R3D_EHIP.
+ * out/lse overlapping an input, a workspace that is NULL, too small, misaligned or
+ * overlapping a tensor), R3D_EUNSUPPORTED (D, dtype, or for R3D_BF16 an Sq or Skv
+ * above 2^31 - 1024: that kernel indexes rows in 32 bits), R3D_EHIP.
  */
 R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                          int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                         int64_t kv_chunk, int32_t dtype, void* stream);
+                         int64_t kv_chunk, int32_t dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * r3d_attn_fwd_workspace_size — bytes of workspace r3d_attn_fwd needs for these
+ * arguments on the CURRENT device (the key-split decision depends on its number of
+ * compute units); r3d_attn_fwd_bshd needs at most as much.  Writes *bytes; performs
+ * no device work and allocates nothing.
+ * Errors: R3D_EINVAL (sizes <= 0, kv_chunk < 0, NULL bytes, overflow),
+ * R3D_EUNSUPPORTED (dtype).
+ */
+R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                        int64_t kv_chunk, int32_t dtype, size_t* bytes);
 
 /*
  * r3d_attn_fwd_bshd — r3d_attn_fwd with the output written token-major:
- *   out : [B, Sq, H, D] (everything else, lse included, as in r3d_attn_fwd).
+ *   out : [B, Sq, H, D] (everything else, lse and workspace included, as in
+ *         r3d_attn_fwd).
  * This is the inverse of the [B, S, H, D] -> [B, H, S, D] re-layout done by
  * r3d_joint_concat_permute, i.e. the local form of the Ulysses output
  * all-to-all that returns the head-sharded result to sequence order (xDiT PR
@@ -189,31 +205,40 @@ R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
  */
 R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                              int64_t kv_chunk, int32_t dtype, void* stream);
+                              int64_t kv_chunk, int32_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
- * r3d_attn_fwd_constmax — r3d_attn_fwd (bf16, out [B, H, Sq, D]) whose softmax
- * reference is a per-row bound fixed before any key is read instead of the
- * running max: the kernel of "Context Parallelism in vLLM Omni Neuron",
+ * r3d_attn_fwd_constmax — r3d_attn_fwd (bf16, out [B, H, Sq, D], one chunk) whose
+ * softmax reference is a per-row bound fixed before any key is read instead of
+ * the running max: the kernel of "Context Parallelism in vLLM Omni Neuron",
  * §Related information (ring_attention_const_max_fwd: "softmax max is a
  * runtime bound"), where a known bound lets K/V chunks be consumed in any
  * order with no rescaling — chunk partials simply add, no log-sum-exp merge.
  * The bound is Cauchy-Schwarz:  m_i = |scale| |q_i| max_j |k_j|  >=  every
- * logit of row i; max_j |k_j| per head is computed by a pre-pass into the
- * workspace.  p = e^(s - m_i) <= 1, out = sum p v / sum p,
- * lse = m_i + ln(sum p): the same function as r3d_attn_fwd while the bound
- * exceeds the row's true max by less than about 87 (fp32's exponent range;
- * beyond it every p of a row underflows and the row comes out NaN).
- *   kmax_ws : DEVICE fp32 workspace of B*H values, 4-byte aligned, overlapping
- *             nothing else; on return it holds max_j |k_j|^2 per (b, h).
+ * logit of row i; p = e^(s - m_i) <= 1, out = sum p v / sum p,
+ * lse = m_i + ln(sum p).  Where the bound exceeds a row's true maximum by more
+ * than fp32's exponent range can carry (the row sum falls below 2^-100, or the
+ * output is not finite), the block tile holding that row is recomputed inside
+ * the same call with the running-max reference, so every row gets
+ * r3d_attn_fwd's result: no row comes back silently underflowed.
+ *   workspace, workspace_bytes : device scratch of at least
+ *             r3d_attn_fwd_constmax_workspace_size(...) bytes, 16-byte aligned,
+ *             overlapping no tensor of the call (per-head statistics of K and V,
+ *             and one flag per wave of every block tile).
  *   dtype   : R3D_BF16 only.  Other arguments as r3d_attn_fwd (no kv_chunk:
  *             with a fixed reference the chunking does not change the result).
- * Errors: as r3d_attn_fwd, plus R3D_EINVAL for the workspace and
- * R3D_EUNSUPPORTED for fp32.
+ * Errors: as r3d_attn_fwd, and R3D_EUNSUPPORTED for fp32.
  */
 R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
-                                  float* kmax_ws, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                                  float scale, int32_t dtype, void* stream);
+                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                                  int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* r3d_attn_fwd_constmax_workspace_size — bytes of workspace r3d_attn_fwd_constmax
+ * needs for these sizes (writes *bytes; no device work).  Errors as
+ * r3d_attn_fwd_workspace_size, and R3D_EUNSUPPORTED for fp32. */
+R3D_API int r3d_attn_fwd_constmax_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                                 int32_t dtype, size_t* bytes);
 
 /*
  * r3d_lse_merge — combine n partial attention results of the same queries

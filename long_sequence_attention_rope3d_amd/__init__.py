@@ -11,9 +11,17 @@ long_sequence_attention_rope3d_amd/build.py``).
 
 Calls (same names as the C entry points without the ``r3d_`` prefix):
   rope3d_apply(x, grid, split, theta=10000.0, out=None)
-  joint_concat_permute(segs, rope=None, out=None)
-  attn_fwd(q, k, v, scale=None, kv_chunk=0, out=None, lse=None, return_lse=True)
+  joint_concat_permute(segs, rope=None, out=None, norm=None, eps=1e-6)
+  attn_fwd(q, k, v, scale=None, kv_chunk=0, out=None, lse=None, return_lse=True,
+           out_layout="bhsd", workspace=None)
+  attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, dtype)
+  attn_fwd_constmax(q, k, v, scale=None, out=None, lse=None, workspace=None)
+  attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, dtype)
   lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None)
+The attention calls take the device scratch the library needs as a
+caller-owned ``workspace`` (a uint8 device tensor of at least the queried
+size); when none is given the binding allocates one with torch (its caching
+allocator, in the call's stream order).
 """
 from __future__ import annotations
 
@@ -25,8 +33,9 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "lse_merge", "joint_attention", "Rope3D",
-           "library_path", "R3D_OK", "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
+__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_constmax",
+           "attn_fwd_constmax_workspace_size", "lse_merge", "joint_attention", "Rope3D", "library_path", "R3D_OK",
+           "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "librope3d_attn.so")
@@ -57,12 +66,16 @@ def _load():
                                              ctypes.POINTER(_RopeDesc), P]
     lib.r3d_joint_concat_permute_qknorm.argtypes = [P, P, I32, P, ctypes.c_double, P, I32, I64, I64, I64,
                                                     ctypes.POINTER(_RopeDesc), P]
-    lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P]
+    SZ = ctypes.c_size_t
+    lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P, SZ, P]
     lib.r3d_attn_fwd_bshd.argtypes = lib.r3d_attn_fwd.argtypes
-    lib.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]
+    lib.r3d_attn_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
+    lib.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, P, SZ, P]
+    lib.r3d_attn_fwd_constmax_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
     lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
     for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_joint_concat_permute_qknorm",
-              "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_attn_fwd_constmax", "r3d_lse_merge"):
+              "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
+              "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     lib.r3d_last_error.restype = ctypes.c_char_p
     lib.r3d_last_error.argtypes = []
@@ -93,6 +106,9 @@ def _check(status: int, what: str) -> None:
     if status in (R3D_EINVAL, R3D_EUNSUPPORTED):
         raise ValueError(f"{what}: {msg}")
     raise RuntimeError(f"{what}: {msg} (status {status})")
+
+
+_DTYPES = {torch.float32: _F32, torch.bfloat16: _BF16}
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -185,13 +201,44 @@ def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = 
     return out
 
 
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> Tuple[Optional[int], int]:
+    """(pointer, bytes) of the call's workspace: the caller's tensor, or a new
+    uint8 tensor from torch's caching allocator (stream-ordered reuse)."""
+    if ws is None:
+        if need == 0:
+            return None, 0
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def attn_fwd_workspace_size(B: int, H: int, Sq: int, Skv: int, D: int, kv_chunk: int,
+                            dtype: torch.dtype) -> int:
+    """Bytes of workspace attn_fwd needs on the current device (r3d_attn_fwd_workspace_size)."""
+    n = ctypes.c_size_t(0)
+    _check(_lib.r3d_attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, _DTYPES[dtype], ctypes.byref(n)),
+           "attn_fwd_workspace_size")
+    return int(n.value)
+
+
+def attn_fwd_constmax_workspace_size(B: int, H: int, Sq: int, Skv: int, D: int, dtype: torch.dtype) -> int:
+    """Bytes of workspace attn_fwd_constmax needs (r3d_attn_fwd_constmax_workspace_size)."""
+    n = ctypes.c_size_t(0)
+    _check(_lib.r3d_attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, _DTYPES[dtype], ctypes.byref(n)),
+           "attn_fwd_constmax_workspace_size")
+    return int(n.value)
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
              kv_chunk: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             return_lse: bool = True, out_layout: str = "bhsd"):
+             return_lse: bool = True, out_layout: str = "bhsd", workspace: Optional[torch.Tensor] = None):
     """Blockwise non-causal attention. q [B,H,Sq,D], k/v [B,H,Skv,D] ->
     (out, lse [B,H,Sq] fp32 natural log) — or out alone if return_lse is False
     and no lse buffer is given.  out is [B,H,Sq,D] (out_layout="bhsd") or
-    token-major [B,Sq,H,D] (out_layout="bshd", r3d_attn_fwd_bshd)."""
+    token-major [B,Sq,H,D] (out_layout="bshd", r3d_attn_fwd_bshd).
+    ``workspace``: device scratch of at least attn_fwd_workspace_size(...)
+    bytes (allocated through torch if None)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
     if out_layout not in ("bhsd", "bshd"):
@@ -214,9 +261,11 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
     fn = _lib.r3d_attn_fwd if out_layout == "bhsd" else _lib.r3d_attn_fwd_bshd
+    need = attn_fwd_workspace_size(B, H, Sq, Skv, D, int(kv_chunk), q.dtype) if workspace is None else 0
+    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     _check(fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
               _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
-              float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd")
+              float(scale), int(kv_chunk), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)), "attn_fwd")
     return (out, lse) if lse is not None else out
 
 
@@ -224,8 +273,10 @@ def attn_fwd_constmax(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, return_lse: bool = True):
     """attn_fwd (bf16, [B,H,Sq,D]) with the softmax reference fixed per row at the
-    Cauchy-Schwarz bound |scale| |q_i| max_j |k_j| (r3d_attn_fwd_constmax).
-    ``workspace``: float32 [B*H] device buffer (allocated here if None)."""
+    Cauchy-Schwarz bound |scale| |q_i| max_j |k_j| (r3d_attn_fwd_constmax); rows
+    the bound leaves underflowed are recomputed with the running max inside the
+    call.  ``workspace``: device scratch of at least
+    attn_fwd_constmax_workspace_size(...) bytes (allocated through torch if None)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
     B, H, Sq, D = q.shape
@@ -244,14 +295,12 @@ def attn_fwd_constmax(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
-    if workspace is None:
-        workspace = torch.empty(B * H, dtype=torch.float32, device=q.device)
-    if workspace.dtype != torch.float32 or workspace.numel() < B * H:
-        raise ValueError("workspace must be float32 with at least B*H values")
+    need = attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, q.dtype) if workspace is None else 0
+    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     _check(_lib.r3d_attn_fwd_constmax(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                      _dev(lse, "lse") if lse is not None else None,
-                                      _dev(workspace, "workspace"), B, H, Sq, Skv, D, float(scale),
-                                      _dtype_code(q), _stream(q)), "attn_fwd_constmax")
+                                      _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                                      float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)),
+           "attn_fwd_constmax")
     return (out, lse) if lse is not None else out
 
 

@@ -61,21 +61,22 @@
 //   holds one query per lane, so rescales and the chunk merge are per-lane
 //   scalars.
 // * Rescale only on a new maximum: when the row max is formed, the reference
-//   moves to it as soon as a step's max exceeds it (kTau = 0), so a row's
-//   largest logit gets p = 2^0 = 1, exact in bf16, and a row dominated by one
+//   moves to it as soon as a step's max exceeds it (no lazy margin), so a
+//   row's largest logit gets p = 2^0 = 1 (2^-off with an offset), exact in bf16, and a row dominated by one
 //   key carries no rounding of that key's weight; steps whose max does not
 //   exceed the reference skip the 64-register rescale of acc.  (A lazy
 //   threshold of 8 was no faster and doubled the worst output error on rows
 //   dominated by one outlier key.)
 // * Bound-gated max: the row max itself is only formed while some row of the
-//   wave has a Cauchy-Schwarz logit bound more than kSlack above its
-//   reference (see the kernel's comment); on typical inputs that is the
+//   wave has a Cauchy-Schwarz logit bound more than the head's slack above
+//   its reference (see the kernel's comment); on typical inputs that is the
 //   first step, and later steps spend no VALU work on the max at all.
 // * The row sum l adds the fp32 p before their bf16 rounding for the PV
 //   product, so lse keeps fp32 accuracy.
 // * Issue priority: every wave keeps the default priority.  Raising it
 //   while a wave issues its MFMAs once paid 1%, but with the VALU trimmed as
 //   it is now it costs 0.5% (52k and long-video alike).
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -113,8 +114,7 @@ constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 static_assert(kAttnMaxSeq + kBN <= INT32_MAX, "key cursor fits in 32 bits");
 constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
-constexpr float kTau = 0.0f;      // rescale threshold, log2 units (0: on every new maximum)
-constexpr float kSlack = 32.0f;   // bound slack under which the row max is skipped, log2 units
+constexpr int kSlackMax = 32;     // largest bound slack under which the row max is skipped, log2 units
 
 template <int D>
 struct Geom {
@@ -275,29 +275,41 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Both variants read kmax2[bh] = max_j |k_j|^2 over the head's keys, which
-// gives each row the Cauchy-Schwarz bound bnd = c |q_i| max_j |k_j| >= every
-// logit of the row (log2 units).
+// Both variants read the head statistics of the pre-pass: max_j |k_j|^2,
+// which gives each row the Cauchy-Schwarz bound bnd = c |q_i| max_j |k_j| >=
+// every logit of the row (log2 units), and max_j |v_j| over all elements.
 //
 // Online (kConstMax false): the reference m is an attained value -- a step's
-// row max, or a chunk's log-sum-exp after the merge -- as in the plain online
-// softmax, but the 16-element row max is only formed while bnd > m + kSlack
-// for some row of the wave.  Once m is within kSlack of the bound, no later
-// logit can exceed it by more than kSlack, so p = 2^(s c - m) <= 2^kSlack
-// without looking at the step's values; only rows whose bound is loose (or
-// the first step, m = -inf) pay for the max.  The result is the online
-// softmax's for every input: the reference only sets the scale of acc and l.
+// row max (plus the offset below), or a chunk's log-sum-exp after the merge --
+// as in the plain online softmax, but the 16-element row max is only formed
+// while bnd > m + slack for some row of the wave.  Once m is within `slack`
+// of the bound, no later logit can exceed it by more than that, so
+// p = 2^(s c - m) <= 2^slack without looking at the step's values; only rows
+// whose bound is loose (or the first step, m = -inf) pay for the max.
+// The slack is per head: the accumulator sums up to chunk + 1 terms of
+// p |v| (the chunk's keys and the carried result), so the slack is capped
+// at E = 126 - ceil(log2(chunk + 1)) - floor(log2(max |v|)), which keeps
+// |acc| below 2^127 (fp32 ends at 2^128): min(32, E).  Where even p <= 1
+// would not (E < 0: |v| near the top of bf16's range), the reference is held
+// `off` = -E above the row's max -- a moved reference is max + off, a carried
+// chunk result enters at weight 2^-off -- so every p <= 2^E.  For ordinary
+// inputs E >= 32 and off = 0.  Either way the reference only sets the scale
+// of acc and l: the result is the online softmax's for every finite input,
+// without its overflow for very large V.
 //
 // kConstMax: the reference is the bound itself, fixed before any key is read:
 // no max reduction, no rescale, and chunk partials simply add.  Exact as long
 // as the bound exceeds the row's true max by less than fp32's exponent range
-// (about 87 in natural-log units); opt-in.
+// (about 87 in natural-log units); each wave flags, per block tile, rows whose
+// row sum fell below 2^-100 or whose output is not finite, and a second
+// launch of the online kernel (fix_flags) recomputes exactly those tiles.
 template <int D, bool kConstMax>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
-    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ kmax2,
-    int n_split, int64_t split_len, int out_f32) {
+    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ stats,
+    int n_split, int64_t split_len, int out_f32, int chunk_bits, int* __restrict__ flags_out,
+    const int* __restrict__ fix_flags) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
   // K/V stage buffers in one array, K stages first: [K_0 .. K_{kStages-1} | V_0 .. V_{kStages-1}].
@@ -330,6 +342,13 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31, hf = lane >> 5;
+  // Recompute pass after the constant-max kernel: only tiles that some wave
+  // flagged.  Every wave reads the same flags, so the whole block leaves
+  // together, before its first barrier.
+  if (!kConstMax && fix_flags) {
+    const int f = lane < kWaves ? fix_flags[(int64_t)logical * kWaves + lane] : 0;
+    if (__ballot(f != 0) == 0) return;
+  }
   const int qrow = qt * kBM + wave * 32 + r32;  // < Sq + kBM <= 2^31
   const int sq = (int)Sq;
   const uint16_t* kb = k + bh * Skv * D;
@@ -375,10 +394,41 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
 #pragma unroll
   for (int b = 0; b < G::kDBlk; ++b) oacc[b] = f32x16{};
   // Running state: acc (oacc), reference m and per-lane partial sum l, log2
-  // domain; thr = (m + kTau) / c, the raw logit above which the reference
-  // must move while the row max is being formed.
+  // domain; thr = (m - off) / c, the raw logit above which the reference
+  // must move while the row max is being formed (a moved reference is
+  // max + off: the reference moves on every new maximum).
   float m_run = -INFINITY, l_run = 0.f, thr = -INFINITY;
   const float inv_c = 1.0f / c;
+  // Head statistics: the pre-pass left kStatParts (= 64, one per lane)
+  // partial maxima of |k_j|^2 and of |v| per head; a butterfly gives every
+  // lane the maxima, made wave-uniform.
+  float kmax2, vabs_max;
+  {
+    static_assert(kStatParts == 64, "one partial per lane");
+    float a = stats[bh * kStatParts + lane];
+    float b = stats[((int64_t)(n_blocks / (n_split * n_qt)) + bh) * kStatParts + lane];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      a = fmaxf(a, __shfl_xor(a, o));
+      b = fmaxf(b, __shfl_xor(b, o));
+    }
+    kmax2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a)));
+    vabs_max = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b)));
+  }
+  // Per-head slack and reference offset (see the kernel's comment):
+  // E = 126 - chunk_bits - floor(log2 max|v|), slack = min(32, E),
+  // off = max(0, -E); a non-finite V (exponent field 255) keeps the plain
+  // online softmax's p <= 1.
+  float slack, off, carry;
+  {
+    const int ex = (int)((__float_as_uint(vabs_max) >> 23) & 0xff);
+    int e_max = 126 - chunk_bits - (ex == 0 ? -127 : ex - 127);
+    if (ex == 255) e_max = 0;
+    slack = (float)(e_max < kSlackMax ? e_max : kSlackMax);
+    const int off_i = e_max < 0 ? -e_max : 0;  // <= 128 + 31 - 126 = 33: 2^-off is a normal float
+    off = (float)off_i;
+    carry = __int_as_float((127 - off_i) << 23);  // 2^-off exactly
+  }
   // The row's logit bound: |q_i|^2 from the Q fragments (each lane half holds
   // half of the row) times max_j |k_j|^2.
   float bnd;
@@ -392,12 +442,12 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         qq = fmaf(x, x, qq);
       }
     qq = sum_halves(qq);
-    bnd = c * sqrtf(qq * kmax2[bh]);
+    bnd = c * sqrtf(qq * kmax2);
   }
   if constexpr (kConstMax) m_run = bnd;  // the fixed reference
   // Wave-uniform: some row of the wave still needs its row max formed.
   bool need_max = true;
-  auto update_need_max = [&]() { need_max = __ballot(bnd > m_run + kSlack) != 0; };
+  auto update_need_max = [&]() { need_max = __ballot(bnd > m_run + slack) != 0; };
 
   const int first_cend = (kv_end - kv_begin > chunk32) ? kv_begin + chunk32 : kv_end;
   // pf: the next tile to prefetch.  Prologue: tiles 0 and 1 in flight, wait for tile 0.
@@ -491,7 +541,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         if (__builtin_expect(__ballot(mx > thr) != 0, 0)) {
           mx = max_halves(mx);
           const bool up = mx > thr;
-          const float m_new = up ? mx * c : m_run;
+          const float m_new = up ? fmaf(mx, c, off) : m_run;
           alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where the row kept it, 0 from m = -inf
           m_run = m_new;
           moved = true;
@@ -525,7 +575,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= alpha;
-        thr = (m_run + kTau) * inv_c;
+        thr = (m_run - off) * inv_c;
         update_need_max();
       }
       l_run += ps;
@@ -541,15 +591,20 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     // normalise to (O, L) = (acc / l, m + log2 l), and let the next chunk
     // start from acc = O, m = L, l = 1 -- value O at weight 2^L.  The next
     // chunk's online rescale then forms exactly O 2^(L - L') + O_c 2^(lse_c - L').
+    // (With a reference offset the carried result enters as acc = O 2^-off,
+    // l = 2^-off, m = L + off: the same weight 2^L.  The last chunk keeps O, L.)
     if (!kConstMax && chunk_done) {
+      const bool last = cur.kv0 + n >= kv_end;
+      const float w_carry = last ? 1.0f : carry;
       const float l_tot = sum_halves(l_run);
-      const float inv = 1.0f / l_tot;
+      const float inv = w_carry / l_tot;
 #pragma unroll
       for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
       m_run += log2f(l_tot);
-      thr = (m_run + kTau) * inv_c;
+      if (!last) m_run += off;
+      thr = (m_run - off) * inv_c;
       update_need_max();
-      l_run = hf == 0 ? 1.0f : 0.0f;  // the weight counts once per row (halves are summed)
+      l_run = hf == 0 ? w_carry : 0.0f;  // the weight counts once per row (halves are summed)
     }
     cur.advance(chunk32, kv_end);
   };
@@ -571,9 +626,20 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   if constexpr (kConstMax) {  // one sum over all keys: normalise now
     const float l_tot = sum_halves(l_run);
     const float inv = 1.0f / l_tot;
+    // A row whose sum underflowed (the bound far above its true maximum) or
+    // whose output is not finite is recomputed by the online kernel: the
+    // wave flags its block's tile.  Padding rows (past Sq) have q = 0, p = 1.
+    bool bad = !(l_tot >= 0x1p-100f);
 #pragma unroll
-    for (int b = 0; b < G::kDBlk; ++b) oacc[b] *= inv;
+    for (int b = 0; b < G::kDBlk; ++b) {
+      oacc[b] *= inv;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bad |= !(fabsf(oacc[b][i]) <= 3.40282347e38f);
+    }
     m_run += log2f(l_tot);
+    const bool any_bad = __ballot(bad) != 0;
+    if (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0)
+      flags_out[(int64_t)logical * kWaves + wave] = any_bad ? 1 : 0;
   }
 
   // ---- epilogue: out (bf16, RNE; or fp32 for a key-split partial) and lse (natural log) ----
@@ -616,78 +682,100 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   }
 }
 
-// kmax2[bh] = 0, so that the partial maxima below can be combined by atomic
-// max on the bit patterns of non-negative floats (ordered like the values).
-__global__ void zero_kernel(float* __restrict__ x, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) x[i] = 0.f;
-}
-
-// kmax2[bh] = max_j |k_j|^2 over the head's Skv key rows.  Grid (B*H) x
-// kSplit blocks; block (bh, part) scans rows part, part + kSplit*rows_per_pass
-// ...; kCpr consecutive lanes hold one row's 16-byte chunks.
+// Head statistics for the bound-gated max: per head, kStatParts partial
+// maxima of |k_j|^2 (stats[0 .. B*H*kStatParts)) and of |v| over every
+// element (the next B*H*kStatParts floats).  Grid (B*H) x kStatParts blocks;
+// block (bh, part) scans rows part*kRows + r, stepping kStatParts*kRows;
+// kCpr consecutive lanes hold one row's 16-byte chunks.  Every partial is
+// written (no atomics, nothing to clear first).
 constexpr int kNormThreads = 256;
-constexpr int kNormSplit = 64;
 template <int D>
-__global__ __launch_bounds__(kNormThreads) void key_norm_max_kernel(const uint16_t* __restrict__ k,
-                                                                    float* __restrict__ kmax2, int64_t Skv) {
+__global__ __launch_bounds__(kNormThreads) void head_stats_kernel(const uint16_t* __restrict__ k,
+                                                                  const uint16_t* __restrict__ v,
+                                                                  float* __restrict__ stats, int64_t Skv,
+                                                                  int64_t nbh) {
   constexpr int kCpr = D / 8;
   constexpr int kRows = kNormThreads / kCpr;  // rows per block pass
-  const int64_t bh = blockIdx.x / kNormSplit;
-  const int part = blockIdx.x % kNormSplit;
+  const int64_t bh = blockIdx.x / kStatParts;
+  const int part = blockIdx.x % kStatParts;
   const int t = threadIdx.x, r = t / kCpr, ci = t % kCpr;
   const uint16_t* kb = k + bh * Skv * D;
+  const uint16_t* vb = v + bh * Skv * D;
   float best = 0.f;
-  for (int64_t j = (int64_t)part * kRows + r; j < Skv; j += (int64_t)kNormSplit * kRows) {
+  uint32_t vbest = 0;  // largest |v| as a bf16 bit pattern (magnitudes order like integers)
+  for (int64_t j = (int64_t)part * kRows + r; j < Skv; j += (int64_t)kStatParts * kRows) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(kb + j * D + ci * 8);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(vb + j * D + ci * 8);
     float ss = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float a = __uint_as_float(x[w] << 16), b = __uint_as_float(x[w] & 0xffff0000u);
       ss = fmaf(a, a, fmaf(b, b, ss));
+      vbest = max(vbest, max(y[w] & 0x7fffu, (y[w] >> 16) & 0x7fffu));
     }
 #pragma unroll
     for (int o = kCpr / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
     best = fmaxf(best, ss);
   }
   __shared__ float red[kNormThreads];
+  __shared__ uint32_t vred[kNormThreads];
   red[t] = best;
+  vred[t] = vbest;
   __syncthreads();
   for (int sz = kNormThreads / 2; sz > 0; sz >>= 1) {
-    if (t < sz) red[t] = fmaxf(red[t], red[t + sz]);
+    if (t < sz) {
+      red[t] = fmaxf(red[t], red[t + sz]);
+      vred[t] = max(vred[t], vred[t + sz]);
+    }
     __syncthreads();
   }
-  if (t == 0) atomicMax(reinterpret_cast<unsigned int*>(kmax2 + bh), __float_as_uint(red[0]));
+  if (t == 0) {
+    stats[bh * kStatParts + part] = red[0];
+    stats[(nbh + bh) * kStatParts + part] = __uint_as_float(vred[0] << 16);
+  }
+}
+
+// Smallest b with 2^b >= n + 1 (n >= 0): the bit count of the accumulation
+// length bound used for the per-head slack.
+int bits_for(int64_t n) {
+  int b = 0;
+  while (b < 62 && (int64_t(1) << b) < n + 1) ++b;
+  return b;
+}
+
+// The head statistics pre-pass (reads K and V once) into stats.
+hipError_t launch_head_stats(const uint16_t* kp, const uint16_t* vp, float* stats, int64_t B, int64_t H,
+                             int64_t Skv, int64_t D, hipStream_t stream) {
+  const int64_t nbh = B * H;
+  if (D == 64)
+    head_stats_kernel<64><<<(unsigned)(nbh * kStatParts), kNormThreads, 0, stream>>>(kp, vp, stats, Skv, nbh);
+  else
+    head_stats_kernel<128><<<(unsigned)(nbh * kStatParts), kNormThreads, 0, stream>>>(kp, vp, stats, Skv, nbh);
+  return hipGetLastError();
 }
 
 template <bool kConstMax>
-hipError_t launch_attn_bf16_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                                 int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                                 bool out_bshd, float* kmax2, int n_split, int64_t split_len, bool out_f32,
-                                 hipStream_t stream) {
+hipError_t launch_attn_kernel(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                              int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
+                              bool out_bshd, const float* stats, int n_split, int64_t split_len, bool out_f32,
+                              int* flags_out, const int* fix_flags, hipStream_t stream) {
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
   const int n_blocks = (int)(B * H * n_split * n_qt);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+  // Longest run of keys accumulated without a merge: a chunk, within a split.
+  const int chunk_bits = bits_for(std::min(std::min(kv_chunk, Skv), n_split > 1 ? split_len : Skv));
   const auto* qp = static_cast<const uint16_t*>(q);
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
-  {
-    const int64_t nbh = B * H;
-    zero_kernel<<<(unsigned)((nbh + 255) / 256), 256, 0, stream>>>(kmax2, nbh);
-    if (D == 64)
-      key_norm_max_kernel<64><<<(unsigned)(nbh * kNormSplit), kNormThreads, 0, stream>>>(kp, kmax2, Skv);
-    else
-      key_norm_max_kernel<128><<<(unsigned)(nbh * kNormSplit), kNormThreads, 0, stream>>>(kp, kmax2, Skv);
-  }
   if (D == 64)
     attn_bf16_kernel<64, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2, n_split,
-        split_len, out_f32 ? 1 : 0);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, stats, n_split,
+        split_len, out_f32 ? 1 : 0, chunk_bits, flags_out, fix_flags);
   else
     attn_bf16_kernel<128, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, kmax2, n_split,
-        split_len, out_f32 ? 1 : 0);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, stats, n_split,
+        split_len, out_f32 ? 1 : 0, chunk_bits, flags_out, fix_flags);
   return hipGetLastError();
 }
 
@@ -698,8 +786,7 @@ bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq) {
     return blocks > 0 && blocks <= (int64_t(1) << 31) - 1 && blocks * threads < (int64_t(1) << 32);
   };
   const int64_t nbh = B * H;
-  return fits((nbh + 255) / 256, 256) && fits(nbh * kNormSplit, kNormThreads) &&
-         fits(nbh * ((Sq + kBM - 1) / kBM), kThreads);
+  return fits(nbh * kStatParts, kNormThreads) && fits(nbh * ((Sq + kBM - 1) / kBM), kThreads);
 }
 
 int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
@@ -740,19 +827,34 @@ int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t k
   return best;
 }
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, float* kmax2,
+int64_t attn_bf16_query_tiles(int64_t Sq) { return (Sq + kBM - 1) / kBM; }
+
+int attn_bf16_waves() { return kWaves; }
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, float* stats,
                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                             int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len, bool out_f32,
                             hipStream_t stream) {
-  return launch_attn_bf16_impl<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, kmax2,
-                                      n_split, split_len, out_f32, stream);
+  hipError_t e = launch_head_stats(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), stats, B, H,
+                                   Skv, D, stream);
+  if (e != hipSuccess) return e;
+  return launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, stats, n_split,
+                                   split_len, out_f32, nullptr, nullptr, stream);
 }
 
 hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
-                                     float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                                     float scale, hipStream_t stream) {
-  return launch_attn_bf16_impl<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, kmax2, 1, Skv, false,
-                                     stream);
+                                     float* stats, int* flags, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                     int64_t D, float scale, hipStream_t stream) {
+  hipError_t e = launch_head_stats(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), stats, B, H,
+                                   Skv, D, stream);
+  if (e != hipSuccess) return e;
+  e = launch_attn_kernel<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, 1, Skv, false, flags,
+                               nullptr, stream);
+  if (e != hipSuccess) return e;
+  // Recompute the flagged tiles with the online reference (one chunk: the
+  // same function; blocks of clean tiles return at once).
+  return launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, 1, Skv, false,
+                                   nullptr, flags, stream);
 }
 
 }  // namespace r3d

@@ -12,8 +12,6 @@
 #include <map>
 #include <mutex>
 #include <string>
-#include <tuple>
-#include <utility>
 
 #include "launch.h"
 
@@ -232,38 +230,7 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
 }
 
 namespace {
-// Library-owned device workspaces of the bf16 attention path, one buffer per
-// (device, stream, kind), so calls on one stream use them in stream order and
-// calls on different streams never share one.  Kinds: kHeadNorms, the
-// per-head largest squared key norm (B*H floats, for the bound-gated max);
-// kSplitParts, the fp32 partials (O, lse) of a key-split launch.  Allocated
-// on first use and grown when a call needs more (after that stream has
-// drained the old buffer); kept until the process ends.
-enum WsKind { kHeadNorms = 0, kSplitParts = 1 };
-hipError_t stream_workspace(hipStream_t stream, WsKind kind, size_t bytes, void** ws) {
-  static std::mutex mu;
-  static std::map<std::tuple<int, hipStream_t, int>, std::pair<void*, size_t>> cache;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  auto& slot = cache[{dev, stream, (int)kind}];
-  if (slot.second < bytes) {
-    if (slot.first) {
-      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return e;
-      if ((e = hipFree(slot.first)) != hipSuccess) return e;
-      slot = {nullptr, 0};
-    }
-    const size_t cap = std::max<size_t>(bytes, 16384);
-    void* p = nullptr;
-    if ((e = hipMalloc(&p, cap)) != hipSuccess) return e;
-    slot = {p, cap};
-  }
-  *ws = slot.first;
-  return hipSuccess;
-}
-
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; 0 if unknown).
 int device_cus() {
   static std::mutex mu;
   static std::map<int, int> cus;
@@ -278,117 +245,181 @@ int device_cus() {
   return n;
 }
 
+constexpr int64_t kWsAlign = 256;  // each workspace region starts on a 256-byte boundary
+int64_t ws_round(int64_t bytes) { return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Validation shared by every attention entry point (q, k, v, out, lse and the
+// sizes); the workspace is checked by the caller of this.
+int check_attn_args(const char* what, const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                    int32_t dtype, int64_t& nq, int64_t& nk, int64_t& bhq) {
+  const int es = elt_size(dtype);
+  if (!es) return fail(R3D_EUNSUPPORTED, "%s: unknown dtype %d", what, dtype);
+  if (!q || !k || !v || !out) return fail(R3D_EINVAL, "%s: NULL tensor pointer", what);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(R3D_EINVAL, "%s: pointers must be 16-byte aligned", what);
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
+    return fail(R3D_EINVAL, "%s: B, H, Sq, Skv, D must be > 0", what);
+  if (!std::isfinite(scale)) return fail(R3D_EINVAL, "%s: scale must be finite", what);
+  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "%s: D=%lld (supported: 64, 128)", what, (long long)D);
+  if (dtype == R3D_BF16 && (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq))
+    return fail(R3D_EUNSUPPORTED, "%s: Sq=%lld, Skv=%lld (bf16: at most %lld each)", what, (long long)Sq,
+                (long long)Skv, (long long)r3d::kAttnMaxSeq);
+  if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
+    return fail(R3D_EINVAL, "%s: tensor too large", what);
+  product(bhq, {B, H, Sq});
+  if (dtype == R3D_BF16 ? !r3d::attn_bf16_launches_fit(B, H, Sq) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
+    return fail(R3D_EINVAL, "%s: B*H*Sq too large for one launch", what);
+  const void* ins[3] = {q, k, v};
+  const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(out, nq * es, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "%s: out overlaps an input", what);
+    if (lse && overlap(lse, bhq * 4, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "%s: lse overlaps an input", what);
+  }
+  if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "%s: lse overlaps out", what);
+  return R3D_OK;
+}
+
+// The workspace must hold `need` bytes, be 16-byte aligned and overlap no
+// tensor of the call.
+int check_workspace(const char* what, const void* ws, size_t ws_bytes, int64_t need, const void* q,
+                    const void* k, const void* v, const void* out, const float* lse, int64_t nq, int64_t nk,
+                    int64_t bhq, int es) {
+  if (need == 0) return R3D_OK;
+  if (!ws) return fail(R3D_EINVAL, "%s: NULL workspace (this call needs %lld bytes)", what, (long long)need);
+  if (!aligned16(ws)) return fail(R3D_EINVAL, "%s: workspace must be 16-byte aligned", what);
+  if (ws_bytes < (size_t)need)
+    return fail(R3D_EINVAL, "%s: workspace of %llu bytes, this call needs %lld", what,
+                (unsigned long long)ws_bytes, (long long)need);
+  const void* ts[5] = {q, k, v, out, lse};
+  const int64_t tb[5] = {nq * es, nk * es, nk * es, nq * es, lse ? bhq * 4 : 0};
+  for (int i = 0; i < 5; ++i)
+    if (overlap(ws, need, ts[i], tb[i])) return fail(R3D_EINVAL, "%s: workspace overlaps a tensor", what);
+  return R3D_OK;
+}
+
+// Workspace plan of a bf16 attn_fwd call: the head statistics, then (for a
+// key-split launch) the fp32 partials n_split x rows x (D + 1).
+struct AttnPlan {
+  int n_split = 1;
+  int64_t split_len = 0;
+  int64_t stats_bytes = 0, parts_bytes = 0;
+  int64_t total() const { return stats_bytes + parts_bytes; }
+};
+
+AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype,
+                   bool out_bshd) {
+  AttnPlan p;
+  p.split_len = Skv;
+  if (dtype != R3D_BF16) return p;  // the fp32 kernel needs no workspace
+  const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
+  p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
+  if (!out_bshd) p.n_split = r3d::attn_bf16_key_split(B, H, Sq, Skv, chunk, device_cus(), &p.split_len);
+  if (p.n_split > 1) p.parts_bytes = ws_round(p.n_split * B * H * Sq * (D + 1) * 4);
+  return p;
+}
+
+int64_t constmax_flags_ints(int64_t B, int64_t H, int64_t Sq) {
+  return B * H * r3d::attn_bf16_query_tiles(Sq) * r3d::attn_bf16_waves();
+}
+
 // Shared by both output layouts: the validation is identical (out has the
 // same number of elements either way).
 int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
                   int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk, int32_t dtype,
-                  bool out_bshd, void* stream) {
-  const int es = elt_size(dtype);
-  if (!es) return fail(R3D_EUNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
-  if (!q || !k || !v || !out) return fail(R3D_EINVAL, "attn_fwd: NULL tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
-    return fail(R3D_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
-  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
-    return fail(R3D_EINVAL, "attn_fwd: B, H, Sq, Skv, D must be > 0");
-  if (kv_chunk < 0) return fail(R3D_EINVAL, "attn_fwd: kv_chunk=%lld < 0", (long long)kv_chunk);
-  if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
-  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
-  if (dtype == R3D_BF16 && (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq))
-    return fail(R3D_EUNSUPPORTED, "attn_fwd: Sq=%lld, Skv=%lld (bf16: at most %lld each)", (long long)Sq,
-                (long long)Skv, (long long)r3d::kAttnMaxSeq);
+                  void* workspace, size_t workspace_bytes, bool out_bshd, void* stream) {
   int64_t nq, nk, bhq;
-  if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
-    return fail(R3D_EINVAL, "attn_fwd: tensor too large");
-  product(bhq, {B, H, Sq});
-  if (dtype == R3D_BF16 ? !r3d::attn_bf16_launches_fit(B, H, Sq) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
-    return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
-  const void* ins[3] = {q, k, v};
-  const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
-  for (int i = 0; i < 3; ++i) {
-    if (overlap(out, nq * es, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: out overlaps an input");
-    if (lse && overlap(lse, bhq * 4, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: lse overlaps an input");
-  }
-  if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "attn_fwd: lse overlaps out");
+  int st = check_attn_args("attn_fwd", q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
+  if (st != R3D_OK) return st;
+  if (kv_chunk < 0) return fail(R3D_EINVAL, "attn_fwd: kv_chunk=%lld < 0", (long long)kv_chunk);
+  const AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, out_bshd);
+  st = check_workspace("attn_fwd", workspace, workspace_bytes, plan.total(), q, k, v, out, lse, nq, nk, bhq,
+                       elt_size(dtype));
+  if (st != R3D_OK) return st;
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
+  const hipStream_t strm = (hipStream_t)stream;
   hipError_t e;
   if (dtype == R3D_BF16) {
-    const hipStream_t st = (hipStream_t)stream;
-    void* norms = nullptr;
-    e = stream_workspace(st, kHeadNorms, (size_t)(B * H) * sizeof(float), &norms);
-    // Few query tiles (a shard's shape): split the keys over several blocks per
-    // tile and merge the fp32 partials, so the grid fills the CUs.
-    int64_t split_len = Skv;
-    const int n_split = out_bshd ? 1 : r3d::attn_bf16_key_split(B, H, Sq, Skv, chunk, device_cus(), &split_len);
-    if (e == hipSuccess && n_split > 1) {
-      const int64_t rows = bhq;
-      void* parts = nullptr;
-      e = stream_workspace(st, kSplitParts, (size_t)(n_split * rows * (D + 1)) * sizeof(float), &parts);
-      if (e == hipSuccess) {
-        float* o_parts = static_cast<float*>(parts);
-        float* l_parts = o_parts + n_split * rows * D;
-        e = r3d::launch_attn_bf16(q, k, v, o_parts, l_parts, static_cast<float*>(norms), B, H, Sq, Skv, D, scale,
-                                  chunk, false, n_split, split_len, true, st);
-        if (e == hipSuccess) e = r3d::launch_lse_merge(o_parts, l_parts, n_split, false, out, lse, true, rows, D, st);
-      }
-    } else if (e == hipSuccess) {
-      e = r3d::launch_attn_bf16(q, k, v, out, lse, static_cast<float*>(norms), B, H, Sq, Skv, D, scale, chunk,
-                                out_bshd, 1, Skv, false, st);
+    float* stats = static_cast<float*>(workspace);
+    if (plan.n_split > 1) {
+      // Few query tiles (a shard's shape): the keys are split over several
+      // blocks per tile, and the fp32 partials merged.
+      float* o_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.stats_bytes);
+      float* l_parts = o_parts + plan.n_split * bhq * D;
+      e = r3d::launch_attn_bf16(q, k, v, o_parts, l_parts, stats, B, H, Sq, Skv, D, scale, chunk, false,
+                                plan.n_split, plan.split_len, true, strm);
+      if (e == hipSuccess)
+        e = r3d::launch_lse_merge(o_parts, l_parts, plan.n_split, false, out, lse, true, bhq, D, strm);
+    } else {
+      e = r3d::launch_attn_bf16(q, k, v, out, lse, stats, B, H, Sq, Skv, D, scale, chunk, out_bshd, 1, Skv, false,
+                                strm);
     }
   } else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
-                             D, scale, chunk, out_bshd, (hipStream_t)stream);
+                             D, scale, chunk, out_bshd, strm);
   return hip_status(e, "attn_fwd");
+}
+
+int ws_size_out(const char* what, int64_t need, size_t* bytes) {
+  if (!bytes) return fail(R3D_EINVAL, "%s: NULL result pointer", what);
+  *bytes = (size_t)need;
+  return ok();
 }
 }  // namespace
 
+R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                                        int32_t dtype, size_t* bytes) {
+  const int es = elt_size(dtype);
+  if (!es) return fail(R3D_EUNSUPPORTED, "attn_fwd_workspace_size: unknown dtype %d", dtype);
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0 || kv_chunk < 0)
+    return fail(R3D_EINVAL, "attn_fwd_workspace_size: B, H, Sq, Skv, D must be > 0 and kv_chunk >= 0");
+  int64_t bhq;
+  if (!product(bhq, {B, H, Sq, D + 1}) || bhq > kMaxElems)
+    return fail(R3D_EINVAL, "attn_fwd_workspace_size: sizes too large");
+  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, false).total(), bytes);
+}
+
+R3D_API int r3d_attn_fwd_constmax_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                                 int32_t dtype, size_t* bytes) {
+  if (dtype != R3D_BF16) return fail(R3D_EUNSUPPORTED, "attn_fwd_constmax_workspace_size: bf16 only");
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
+    return fail(R3D_EINVAL, "attn_fwd_constmax_workspace_size: B, H, Sq, Skv, D must be > 0");
+  int64_t bhq;
+  if (!product(bhq, {B, H, Sq}) || bhq > kMaxElems)
+    return fail(R3D_EINVAL, "attn_fwd_constmax_workspace_size: sizes too large");
+  return ws_size_out("attn_fwd_constmax_workspace_size",
+                     ws_round(r3d::attn_stats_floats(B, H) * 4) + ws_round(constmax_flags_ints(B, H, Sq) * 4), bytes);
+}
+
 R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                          int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                         int64_t kv_chunk, int32_t dtype, void* stream) {
-  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, false, stream);
+                         int64_t kv_chunk, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, workspace, workspace_bytes,
+                       false, stream);
 }
 
 R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void* out, float* lse,
                               int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                              int64_t kv_chunk, int32_t dtype, void* stream) {
-  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, true, stream);
+                              int64_t kv_chunk, int32_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, workspace, workspace_bytes,
+                       true, stream);
 }
 
 R3D_API int r3d_attn_fwd_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
-                                  float* kmax_ws, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                                  float scale, int32_t dtype, void* stream) {
+                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                                  int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != R3D_BF16) return fail(R3D_EUNSUPPORTED, "attn_fwd_constmax: bf16 only");
-  if (!kmax_ws || ((uintptr_t)kmax_ws & 3)) return fail(R3D_EINVAL, "attn_fwd_constmax: workspace NULL or misaligned");
-  // q/k/v/out/lse are validated as in r3d_attn_fwd, the workspace on top.
-  if (!q || !k || !v || !out) return fail(R3D_EINVAL, "attn_fwd: NULL tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
-    return fail(R3D_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
-  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0)
-    return fail(R3D_EINVAL, "attn_fwd: B, H, Sq, Skv, D must be > 0");
-  if (!std::isfinite(scale)) return fail(R3D_EINVAL, "attn_fwd: scale must be finite");
-  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd: D=%lld (supported: 64, 128)", (long long)D);
-  if (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq)
-    return fail(R3D_EUNSUPPORTED, "attn_fwd: Sq=%lld, Skv=%lld (bf16: at most %lld each)", (long long)Sq,
-                (long long)Skv, (long long)r3d::kAttnMaxSeq);
-  int64_t nq, nk, bhq, nbh;
-  if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
-    return fail(R3D_EINVAL, "attn_fwd: tensor too large");
-  product(bhq, {B, H, Sq});
-  product(nbh, {B, H});
-  if (!r3d::attn_bf16_launches_fit(B, H, Sq))
-    return fail(R3D_EINVAL, "attn_fwd: B*H*Sq too large for one launch");
-  const int es = 2;
-  const void* ins[3] = {q, k, v};
-  const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};
-  for (int i = 0; i < 3; ++i) {
-    if (overlap(out, nq * es, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: out overlaps an input");
-    if (lse && overlap(lse, bhq * 4, ins[i], in_bytes[i])) return fail(R3D_EINVAL, "attn_fwd: lse overlaps an input");
-    if (overlap(kmax_ws, nbh * 4, ins[i], in_bytes[i]))
-      return fail(R3D_EINVAL, "attn_fwd_constmax: workspace overlaps an input");
-  }
-  if (lse && overlap(lse, bhq * 4, out, nq * es)) return fail(R3D_EINVAL, "attn_fwd: lse overlaps out");
-  if (overlap(kmax_ws, nbh * 4, out, nq * es) || (lse && overlap(kmax_ws, nbh * 4, lse, bhq * 4)))
-    return fail(R3D_EINVAL, "attn_fwd_constmax: workspace overlaps an output");
-  return hip_status(r3d::launch_attn_bf16_constmax(q, k, v, out, lse, kmax_ws, B, H, Sq, Skv, D, scale,
+  int64_t nq, nk, bhq;
+  int st = check_attn_args("attn_fwd_constmax", q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
+  if (st != R3D_OK) return st;
+  const int64_t stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
+  const int64_t need = stats_bytes + ws_round(constmax_flags_ints(B, H, Sq) * 4);
+  st = check_workspace("attn_fwd_constmax", workspace, workspace_bytes, need, q, k, v, out, lse, nq, nk, bhq, 2);
+  if (st != R3D_OK) return st;
+  float* stats = static_cast<float*>(workspace);
+  int* flags = reinterpret_cast<int*>(static_cast<char*>(workspace) + stats_bytes);
+  return hip_status(r3d::launch_attn_bf16_constmax(q, k, v, out, lse, stats, flags, B, H, Sq, Skv, D, scale,
                                                    (hipStream_t)stream),
                     "attn_fwd_constmax");
 }

@@ -58,36 +58,51 @@ hipError_t launch_rope3d(const void* x, void* y, bool bf16, int64_t B, int64_t N
 hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, int64_t H,
                           int64_t D, const RopeArgs& rope, hipStream_t stream);
 
+// Head statistics of the bf16 attention path: kStatParts partial maxima per
+// head of |k_j|^2 and of |v| (2 * B*H*kStatParts floats of workspace).
+constexpr int kStatParts = 64;
+inline int64_t attn_stats_floats(int64_t B, int64_t H) { return 2 * B * H * kStatParts; }
+
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
-// instead of [B, H, Sq, D].  kmax2 is a [B*H] fp32 device workspace (the
-// per-head largest squared key norm, written and read on `stream`).
+// instead of [B, H, Sq, D].  stats is a device workspace of
+// attn_stats_floats(B, H) floats, written by a pre-pass and read by the
+// attention kernel on `stream`.
 // n_split > 1: the keys are split into n_split ranges of split_len keys (a
 // multiple of kv_chunk, or of the 128-key tile when kv_chunk >= Skv), each
 // query tile runs once per range, and out / lse receive the fp32 partials
 // [n_split, B*H*Sq, D] / [n_split, B*H*Sq] (out_f32 true, out_bshd false),
 // for an lse_merge over the n_split parts.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
-                            float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                            float* stats, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                             float scale, int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len,
                             bool out_f32, hipStream_t stream);
+
+// Query tiles per head and waves per block of the bf16 attention kernel (the
+// constant-max variant's flags take query_tiles * waves ints per head).
+int64_t attn_bf16_query_tiles(int64_t Sq);
+int attn_bf16_waves();
 
 // Number of key splits (1: none) for a bf16 attention launch on a device with
 // n_cus compute units, and *split_len: splitting only when the query tiles
 // alone leave the last round of blocks on the CUs mostly empty.
 constexpr int kMaxKeySplit = 8;
 // True when the launches of one bf16 attn_fwd call without a key split (the
-// zeroing and key-norm pre-pass, and the attention grid) each stay within a
-// 1-D grid's 2^31 - 1 blocks and 2^32 work-items.  (A key split is only
-// chosen for grids of fewer than 4 blocks per CU.)
+// statistics pre-pass and the attention grid) each stay within a 1-D grid's
+// 2^31 - 1 blocks and 2^32 work-items.  (A key split is only chosen for
+// grids of fewer than 4 blocks per CU.)
 bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq);
 int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
                         int64_t* split_len);
 
 // attn_fwd with a constant per-row softmax reference (the Cauchy-Schwarz
-// bound from the head's largest key norm); kmax2 is a [B*H] fp32 workspace.
+// bound from the head's largest key norm).  stats as above; flags is a
+// device workspace of B*H*attn_bf16_query_tiles(Sq)*attn_bf16_waves() ints,
+// written by the constant-max kernel (per wave: some row underflowed or is
+// not finite) and read by a second launch of the online kernel that
+// recomputes the flagged tiles.
 hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
-                                     float* kmax2, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                                     float scale, hipStream_t stream);
+                                     float* stats, int* flags, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                     int64_t D, float scale, hipStream_t stream);
 
 // attn_fwd, fp32 path (D = 64 or 128); out_bshd as above.
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,

@@ -30,7 +30,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute",
                                   "r3d_joint_concat_permute_qknorm", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
-                                  "r3d_attn_fwd_constmax", "r3d_lse_merge", "r3d_last_error",
+                                  "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
+                                  "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge", "r3d_last_error",
                                   "r3d_version"])
 
 
@@ -56,24 +57,39 @@ def test_version_string():
 P = ctypes.c_void_p
 I32, I64 = ctypes.c_int32, ctypes.c_int64
 F = ctypes.c_float
-LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P]
+SZ = ctypes.c_size_t
+LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P, SZ, P]
 LIB.r3d_attn_fwd_bshd.argtypes = LIB.r3d_attn_fwd.argtypes
-LIB.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, F, I32, P]
+LIB.r3d_attn_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
+LIB.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I32, P, SZ, P]
+LIB.r3d_attn_fwd_constmax_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
 LIB.r3d_rope3d_apply.argtypes = [P, P, I32, I64, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute.argtypes = [P, P, I32, P, I32, I64, I64, I64, P, P]
 LIB.r3d_joint_concat_permute_qknorm.argtypes = [P, P, I32, P, ctypes.c_double, P, I32, I64, I64, I64, P, P]
 LIB.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
 LIB.r3d_last_error.restype = ctypes.c_char_p
 
-A, B_, C, O, L_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+A, B_, C, O, L_, W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x70000000
 
 
 def _attn(fn="r3d_attn_fwd", **kw):
     a = dict(q=A, k=B_, v=C, out=O, lse=L_, B=1, H=2, Sq=64, Skv=64, D=128, scale=0.125,
-             kv_chunk=0, dtype=1)
+             kv_chunk=0, dtype=1, ws=W, ws_bytes=1 << 24)
     a.update(kw)
     return getattr(LIB, fn)(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Sq"],
-                            a["Skv"], a["D"], a["scale"], a["kv_chunk"], a["dtype"], None)
+                            a["Skv"], a["D"], a["scale"], a["kv_chunk"], a["dtype"], a["ws"], a["ws_bytes"],
+                            None)
+
+
+def _ws_size(fn="r3d_attn_fwd_workspace_size", **kw):
+    a = dict(B=1, H=2, Sq=64, Skv=64, D=128, kv_chunk=0, dtype=1)
+    a.update(kw)
+    n = SZ(12345)
+    args = [a["B"], a["H"], a["Sq"], a["Skv"], a["D"]]
+    if fn == "r3d_attn_fwd_workspace_size":
+        args.append(a["kv_chunk"])
+    st = getattr(LIB, fn)(*args, a["dtype"], ctypes.byref(n))
+    return st, n.value
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -101,13 +117,43 @@ def test_attn_fwd_rejects(fn, kw, status, needle):
     assert needle in LIB.r3d_last_error().decode()
 
 
+def test_attn_fwd_workspace_size():
+    """The bf16 path needs the per-head statistics (2*B*H*64 floats, rounded up to 256
+    bytes); without a GPU no key split is planned, so that is all.  fp32 needs nothing."""
+    st, n = _ws_size(B=3, H=5)
+    assert st == 0 and n == -(-2 * 15 * 64 * 4 // 256) * 256
+    st, n = _ws_size(dtype=0)
+    assert st == 0 and n == 0
+    assert _ws_size(dtype=5)[0] == -2
+    assert _ws_size(Sq=0)[0] == -1 and "> 0" in LIB.r3d_last_error().decode()
+    assert _ws_size(kv_chunk=-1)[0] == -1
+    assert _ws_size(B=1 << 40, H=1 << 20)[0] == -1 and "too large" in LIB.r3d_last_error().decode()
+    assert LIB.r3d_attn_fwd_workspace_size(1, 2, 64, 64, 128, 0, 1, None) == -1
+    # constant-max: statistics + one int flag per wave (12) of every 384-row tile
+    st, n = _ws_size("r3d_attn_fwd_constmax_workspace_size", B=2, H=3, Sq=1000)
+    assert st == 0 and n == -(-2 * 6 * 64 * 4 // 256) * 256 + -(-6 * 3 * 12 * 4 // 256) * 256
+    assert _ws_size("r3d_attn_fwd_constmax_workspace_size", dtype=0)[0] == -2
+
+
+@pytest.mark.parametrize("fn", ["r3d_attn_fwd", "r3d_attn_fwd_bshd"])
+def test_attn_fwd_rejects_bad_workspace(fn):
+    need = _ws_size()[1]
+    assert _attn(fn, ws=None) == -1 and "NULL workspace" in LIB.r3d_last_error().decode()
+    assert _attn(fn, ws_bytes=need - 1) == -1 and f"needs {need}" in LIB.r3d_last_error().decode()
+    assert _attn(fn, ws=W + 8) == -1 and "aligned" in LIB.r3d_last_error().decode()
+    assert _attn(fn, ws=O + 4096) == -1 and "workspace overlaps" in LIB.r3d_last_error().decode()
+    assert _attn(fn, ws=L_ - 64) == -1 and "workspace overlaps" in LIB.r3d_last_error().decode()
+    # argument errors are reported before workspace errors
+    assert _attn(fn, ws=None, D=96) == -2
+
+
 def test_attn_fwd_constmax_rejects():
-    W = 0x70000000
-    def call(ws=W, dtype=1, D=128, out=O, Sq=64, Skv=64):
-        return LIB.r3d_attn_fwd_constmax(A, B_, C, out, L_, ws, 1, 2, Sq, Skv, D, 0.125, dtype, None)
+    def call(ws=W, ws_bytes=1 << 24, dtype=1, D=128, out=O, Sq=64, Skv=64):
+        return LIB.r3d_attn_fwd_constmax(A, B_, C, out, L_, 1, 2, Sq, Skv, D, 0.125, dtype, ws, ws_bytes, None)
     assert call(dtype=0) == -2 and "bf16" in LIB.r3d_last_error().decode()
     assert call(ws=None) == -1 and "workspace" in LIB.r3d_last_error().decode()
     assert call(ws=W + 2) == -1
+    assert call(ws_bytes=100) == -1 and "needs" in LIB.r3d_last_error().decode()
     assert call(ws=O + 64) == -1 and "overlaps" in LIB.r3d_last_error().decode()
     assert call(D=96) == -2
     assert call(out=A) == -1
