@@ -14,7 +14,10 @@
 //                          first (QK-norm: norm_q / norm_k act on the projected
 //                          q, k before they are split into heads and before
 //                          RoPE, same page, §Self-Attention with Context
-//                          Parallelism).
+//                          Parallelism; each of those ops yields a tensor in
+//                          the model dtype, so the norm's output is rounded to
+//                          the storage type before it is rotated, as a stored
+//                          value would be).
 //
 // Layout of the work.  A block owns kTok (with the QK-norm kTokNorm)
 // consecutive tokens of one batch row and all H heads of them.  Per token, the cos/sin of its D/2 pair angles are
@@ -123,47 +126,45 @@ __device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const double2* cs, int ch
   return v;
 }
 
-// QK-norm of one 16-byte chunk, then (cs != nullptr) its rotation: every
-// element x becomes x * r * w (r = 1/sqrt(mean square + eps) of its token,
-// w its channel's weight: wa, wb hold the chunk's channels 0..7, fp32 rows
-// use wa only), the pairs are rotated, all in fp64, and each value is
-// rounded once.
+// QK-norm of one 16-byte chunk: every element x becomes x * r * w (r =
+// 1/sqrt(mean square + eps) of its token, w its channel's weight: wa, wb hold
+// the chunk's channels 0..7, fp32 rows use wa only), correctly rounded to the
+// storage type -- the norm's stored output, which a rotation then reads like
+// any stored value.  bfloat16: y32 = x * r32 * w in fp32 (r32 = (float)r;
+// three roundings, so |y32 - x r w| <= 3 * 2^-24 |y32| <= 3 ulps of y32), then
+// RNE to bfloat16 by v_cvt_pk_bf16_f32.  That is the correctly rounded value
+// unless x r w sits within those 3 ulps of a bfloat16 midpoint (a binary32
+// value with low half 0x8000): lanes whose y32 is within 4 ulps of one, or
+// subnormal, recompute x r w in fp64 and round it exactly (rare: about 9 in
+// 65536 values).  binary32 storage: fp64 arithmetic and one rounding.
 template <bool BF16>
-__device__ __forceinline__ u32x4 norm_rotate_chunk(u32x4 v, double r, float4 wa, float4 wb, const double2* cs,
-                                                   int chunk) {
+__device__ __forceinline__ u32x4 norm_chunk(u32x4 v, double r, float4 wa, float4 wb) {
   const float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
   if constexpr (BF16) {
+    const float r32 = (float)r;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      double x0 = (double)__uint_as_float(v[q] << 16) * r * (double)w[2 * q];
-      double x1 = (double)__uint_as_float(v[q] & 0xffff0000u) * r * (double)w[2 * q + 1];
-      if (cs) {
-        const double2 c = cs[chunk * 4 + q];
-        const double y0 = x0 * c.x - x1 * c.y, y1 = x0 * c.y + x1 * c.x;
-        x0 = y0;
-        x1 = y1;
-      }
-      v[q] = f64x2_to_bf16x2(x0, x1);
+      const float x0 = __uint_as_float(v[q] << 16), x1 = __uint_as_float(v[q] & 0xffff0000u);
+      const float y0 = x0 * r32 * w[2 * q], y1 = x1 * r32 * w[2 * q + 1];
+      const uint32_t u0 = __float_as_uint(y0), u1 = __float_as_uint(y1);
+      const bool slow = (((u0 - 0x7ffcu) & 0xffffu) <= 8u) | (((u1 - 0x7ffcu) & 0xffffu) <= 8u) |
+                        ((u0 & 0x7f800000u) == 0u) | ((u1 & 0x7f800000u) == 0u);
+      if (__builtin_expect(slow, 0))
+        v[q] = f64_to_bf16((double)x0 * r * (double)w[2 * q]) |
+               (f64_to_bf16((double)x1 * r * (double)w[2 * q + 1]) << 16);
+      else
+        v[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{y0, y1}, bf16x2_t));
     }
   } else {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      double x0 = (double)__uint_as_float(v[2 * p]) * r * (double)w[2 * p];
-      double x1 = (double)__uint_as_float(v[2 * p + 1]) * r * (double)w[2 * p + 1];
-      if (cs) {
-        const double2 c = cs[chunk * 2 + p];
-        const double y0 = x0 * c.x - x1 * c.y, y1 = x0 * c.y + x1 * c.x;
-        x0 = y0;
-        x1 = y1;
-      }
-      v[2 * p] = __float_as_uint((float)x0);
-      v[2 * p + 1] = __float_as_uint((float)x1);
-    }
+    for (int p = 0; p < 4; ++p)
+      v[p] = __float_as_uint((float)((double)__uint_as_float(v[p]) * r * (double)w[p]));
   }
   return v;
 }
 
-// Sum of squares of the values in one 16-byte chunk (exact products in fp64).
+// Sum of squares of the values in one 16-byte chunk, in fp64 (each square of
+// a bfloat16 or binary32 value is exact there; the sums round at 2^-53).
 template <bool BF16>
 __device__ __forceinline__ double chunk_sumsq(u32x4 v) {
   double s = 0.0;
@@ -171,13 +172,14 @@ __device__ __forceinline__ double chunk_sumsq(u32x4 v) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const double x0 = (double)__uint_as_float(v[q] << 16), x1 = (double)__uint_as_float(v[q] & 0xffff0000u);
-      s += x0 * x0 + x1 * x1;
+      s = fma(x0, x0, s);
+      s = fma(x1, x1, s);
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const double x = (double)__uint_as_float(v[q]);
-      s += x * x;
+      s = fma(x, x, s);
     }
   }
   return s;
@@ -330,14 +332,18 @@ __global__ __launch_bounds__((threads_per_block<ROPE, NORM>())) void rope_permut
           const int h = h0 + i * hstep;
           float4 na = wa, nb = wb;
           if (i + 1 < nh) wload(h + hstep, na, nb);
-          store(h, norm_rotate_chunk<BF16>(held[i], r, wa, wb, rot ? cs[tl] : nullptr, chunk));
+          u32x4 y = norm_chunk<BF16>(held[i], r, wa, wb);
+          if (rot) y = rotate_chunk<BF16>(y, cs[tl], chunk);
+          store(h, y);
           wa = na;
           wb = nb;
         }
       }
       for (int h = h0 + kHold * hstep; h < H; h += hstep) {
         wload(h, wa, wb);
-        store(h, norm_rotate_chunk<BF16>(src[(int64_t)h * cpr], r, wa, wb, rot ? cs[tl] : nullptr, chunk));
+        u32x4 y = norm_chunk<BF16>(src[(int64_t)h * cpr], r, wa, wb);
+        if (rot) y = rotate_chunk<BF16>(y, cs[tl], chunk);
+        store(h, y);
       }
     } else {
       // Copy / rotate: the held chunks, then any remaining heads.

@@ -7,6 +7,8 @@ may import this package.  It shares no code with the HIP path and never
 imports it.
 
 Composition of the full joint-attention pipeline (``reference_forward``):
+  0. (optional, ``prepare_qkv``) RMS QK-norm of each token's H*D values in
+     fp64, rounded to the storage dtype: the norm's output is a stored tensor.
   1. RoPE in fp64 on the video segment of Q and K ("Context Parallelism in
      vLLM Omni Neuron", §Self-Attention with Context Parallelism: RoPE on
      query and key, never on value).
@@ -243,27 +245,30 @@ def lse_merge(parts, lse_parts):
 
 def prepare_qkv(q_segs, k_segs, v_segs, grid, split, theta, io_dtype, norm_q=None, norm_k=None,
                 eps: float = 1e-6):
-    """Steps 1-3 of the pipeline: optional RMS QK-norm (norm_q / norm_k: None,
-    or one entry per segment, None or the segment's [H*D] weight vector; the
-    statistic is over each token's H*D values), fp64 RoPE on segment 0 of Q
-    and K, one rounding of every changed value to ``io_dtype`` ("bf16" or
-    "f32"), then the joint concat + [B,S,H,D] -> [B,H,S,D] re-layout.  Inputs
-    are fp64 arrays holding the exact values of the stored inputs, one
+    """Steps 1-3 of the pipeline, one stored tensor after each of the page's ops
+    ("Context Parallelism in vLLM Omni Neuron", §Self-Attention with Context
+    Parallelism: q = norm_q(q), then unflatten into heads, then
+    apply_rotary_emb_wan(q, ...), each producing a tensor in the model dtype):
+      * optional RMS QK-norm (norm_q / norm_k: None, or one entry per segment,
+        None or the segment's [H*D] weight vector; the statistic is over each
+        token's H*D values), computed in fp64 and rounded to ``io_dtype``
+        ("bf16" or "f32") -- the stored norm output;
+      * fp64 RoPE of segment 0 of Q and K (from the stored values), rounded
+        to ``io_dtype`` -- the stored rotary output;
+      * the joint concat + [B,S,H,D] -> [B,H,S,D] re-layout.
+    Inputs are fp64 arrays holding the exact values of the stored inputs, one
     [B,S_i,H,D] array per segment, video first.  Returns fp64 q, k, v in
     [B,H,S,D]."""
     def prepared(segs, norms):
         out = []
         for i, s in enumerate(segs):
             x = _f64(s)
-            changed = False
             if norms is not None and norms[i] is not None:
                 B, S, H, D = x.shape
-                x = rms_norm(x.reshape(B, S, H * D), norms[i], eps).reshape(B, S, H, D)
-                changed = True
+                x = round_to(rms_norm(x.reshape(B, S, H * D), norms[i], eps).reshape(B, S, H, D), io_dtype)
             if i == 0:
-                x = rope3d(x, grid, split, theta)
-                changed = True
-            out.append(round_to(x, io_dtype) if changed else x)
+                x = round_to(rope3d(x, grid, split, theta), io_dtype)
+            out.append(x)
         return out
     q = joint_concat_permute(prepared(q_segs, norm_q))
     k = joint_concat_permute(prepared(k_segs, norm_k))

@@ -420,3 +420,98 @@ def test_qknorm_segment_without_weights_is_untouched():
     q0, _, _ = oracle.prepare_qkv(segs, segs, v, grid, sp, THETA, "f32")
     np.testing.assert_array_equal(q1[:, :, 4:], q0[:, :, 4:])
     assert not np.array_equal(q1[:, :, :4], q0[:, :, :4])
+
+
+def _torch_route_qknorm_rope(x, w, eps, grid, split, theta, *, order="norm_first", weight_after=False,
+                             per_head=False, round_between=True):
+    """prepare_qkv's segment-0 Q, built only from torch library pieces: rms_norm over the token's
+    H*D values with the weight, a stored bf16 tensor, RoPE as multiplication of (x_2j + i x_2j+1)
+    by e^(i phi) (torch.polar), a stored bf16 tensor.  The keyword arguments build the plausible
+    wrong compositions the pin must reject."""
+    B, S, H, D = x.shape
+    t = torch.from_numpy(x)
+    wt = torch.from_numpy(w)
+    st = lambda a: a.to(torch.float32).to(torch.bfloat16).to(torch.float64)  # noqa: E731  stored bf16
+
+    def norm(a):
+        if per_head:
+            return torch.nn.functional.rms_norm(a, (D,), eps=eps) * wt.reshape(H, D)
+        return torch.nn.functional.rms_norm(a.reshape(B, S, H * D), (H * D,), weight=None if weight_after else wt,
+                                            eps=eps).reshape(B, S, H, D)
+
+    pos = np.stack(np.unravel_index(np.arange(S), grid), -1)       # (t, h, w) of each token
+    phi = []
+    for a, d in enumerate(split):
+        j = np.arange(d // 2)
+        phi.append(pos[:, a:a + 1] * theta ** (-2.0 * j / d))
+    phi = torch.from_numpy(np.concatenate(phi, -1))                 # [S, D/2]
+    rot = torch.polar(torch.ones_like(phi), phi)
+
+    def rope(a):
+        z = torch.view_as_complex(a.reshape(B, S, H, D // 2, 2).contiguous()) * rot[None, :, None, :]
+        return torch.view_as_real(z).reshape(B, S, H, D)
+
+    if order == "norm_first":
+        y = norm(t)
+        if round_between:
+            y = st(y)
+        y = rope(y)
+        if weight_after:
+            y = y * wt.reshape(H, D)
+    else:                                                            # RoPE, then the norm
+        y = norm(st(rope(t)))
+    return st(y).numpy()
+
+
+def _bf16_ulp(x):
+    ax = np.abs(x)
+    return np.exp2(np.maximum(np.floor(np.log2(np.where(ax > 0, ax, 1.0))), -126) - 7)
+
+
+def test_prepare_qkv_qknorm_matches_torch_route():
+    """Pins the QK-norm composition of prepare_qkv (norm with per-channel weights over the token's
+    H*D values, stored in bf16, then RoPE, stored again) against an independent torch route, on
+    non-unit weights, heads of different scales and a grid with every axis moving.  The bar is the
+    GPU's (within 1 bf16 ulp, >= 99.9% equal: torch's fp64 -> bf16 cast rounds twice).  Each
+    plausible mistake -- RoPE before the norm, the weight applied after the rotation, a per-head
+    statistic, or one rounding of the whole composition -- is shown to fail that bar."""
+    grid, sp = (3, 4, 5), (16, 24, 24)
+    B, H, D = 2, 3, 64
+    S = grid[0] * grid[1] * grid[2]
+    x = RNG.standard_normal((B, S, H, D)) * np.array([0.5, 2.0, 7.0])[None, None, :, None]
+    x = oracle.round_bf16(x)                                         # stored bf16 inputs
+    w = 1.0 + 0.5 * RNG.standard_normal(H * D)
+    joint = oracle.round_bf16(RNG.standard_normal((B, 7, H, D)))
+    eps = 1e-6
+    q, _, _ = oracle.prepare_qkv([x, joint], [x, joint], [x, joint], grid, sp, THETA, "bf16",
+                                 norm_q=[w, None], eps=eps)
+    got = q[:, :, :S].transpose(0, 2, 1, 3)
+
+    def meets_bar(want):
+        d = np.abs(got - want)
+        return bool((d <= _bf16_ulp(want)).all() and (d == 0).mean() >= 0.999)
+
+    assert meets_bar(_torch_route_qknorm_rope(x, w, eps, grid, sp, THETA))
+    for wrong in (dict(order="rope_first"), dict(weight_after=True), dict(per_head=True),
+                  dict(round_between=False)):
+        assert not meets_bar(_torch_route_qknorm_rope(x, w, eps, grid, sp, THETA, **wrong)), wrong
+    # the joint segment without weights is a bit-exact copy
+    np.testing.assert_array_equal(q[:, :, S:], joint.transpose(0, 2, 1, 3))
+
+
+def test_prepare_qkv_qknorm_joint_segment_single_rounding():
+    """A weighted joint segment (not rotated) is the norm's stored output: torch's rms_norm of the
+    token's H*D values, cast to bf16 once."""
+    grid, sp = (1, 2, 3), (0, 32, 32)
+    B, H, D = 1, 4, 64
+    vid = oracle.round_bf16(RNG.standard_normal((B, 6, H, D)))
+    txt = oracle.round_bf16(RNG.standard_normal((B, 9, H, D)) * 3.0)
+    w = 1.0 + 0.3 * RNG.standard_normal(H * D)
+    q, _, _ = oracle.prepare_qkv([vid, txt], [vid, txt], [vid, txt], grid, sp, THETA, "bf16",
+                                 norm_q=[None, w], eps=1e-6)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(txt).reshape(B, 9, H * D), (H * D,),
+                                        weight=torch.from_numpy(w), eps=1e-6)
+    want = want.to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy().reshape(B, 9, H, D)
+    got = q[:, :, 6:].transpose(0, 2, 1, 3)
+    d = np.abs(got - want)
+    assert (d <= _bf16_ulp(want)).all() and (d == 0).mean() >= 0.999
