@@ -191,6 +191,26 @@ R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_
                                         int64_t kv_chunk, int32_t dtype, size_t* bytes);
 
 /*
+ * r3d_attn_fwd_noalloc — r3d_attn_fwd without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Its scratch is a
+ * fixed 16 MiB device array inside the library, one per GPU, held until the process
+ * ends; its address is looked up once per device on the first call.
+ *   Limit: the R3D_BF16 path needs 512 * B * H bytes of per-head statistics, so B*H
+ *   above 32768 is rejected (R3D_EINVAL).  A launch that r3d_attn_fwd would key-split
+ *   runs unsplit when the split's fp32 partials do not fit beside them (the result
+ *   then differs from r3d_attn_fwd's only by rounding).  R3D_F32 uses no scratch.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls whose work
+ *   overlaps on one GPU (different streams, or threads without ordering) race; calls
+ *   in order on one stream are safe.  Nothing in the array needs clearing between
+ *   calls (each call writes all it reads).
+ *   Other arguments, output and errors as r3d_attn_fwd.
+ */
+R3D_API int r3d_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                                 int64_t kv_chunk, int32_t dtype, void* stream);
+
+/*
  * r3d_attn_fwd_bshd — r3d_attn_fwd with the output written token-major:
  *   out : [B, Sq, H, D] (everything else, lse and workspace included, as in
  *         r3d_attn_fwd).

@@ -33,7 +33,8 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_constmax",
+__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_noalloc",
+           "attn_fwd_constmax",
            "attn_fwd_constmax_workspace_size", "lse_merge", "joint_attention", "Rope3D", "library_path", "R3D_OK",
            "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
 
@@ -69,12 +70,14 @@ def _load():
     SZ = ctypes.c_size_t
     lib.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P, SZ, P]
     lib.r3d_attn_fwd_bshd.argtypes = lib.r3d_attn_fwd.argtypes
+    lib.r3d_attn_fwd_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I64, I32, P]
     lib.r3d_attn_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
     lib.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, P, SZ, P]
     lib.r3d_attn_fwd_constmax_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
     lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
     for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_joint_concat_permute_qknorm",
-              "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
+              "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_attn_fwd_noalloc", "r3d_attn_fwd_workspace_size",
+              "r3d_attn_fwd_constmax",
               "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     lib.r3d_last_error.restype = ctypes.c_char_p
@@ -266,6 +269,36 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     _check(fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
               _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
               float(scale), int(kv_chunk), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)), "attn_fwd")
+    return (out, lse) if lse is not None else out
+
+
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                     kv_chunk: int = 0, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = True):
+    """attn_fwd ([B,H,Sq,D] output) through r3d_attn_fwd_noalloc: the library's fixed
+    per-GPU scratch instead of a workspace (no allocation beyond out/lse when the
+    caller passes those)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError("k and v must be [B, H, Skv, D] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, H, Sq, D) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be [B, H, Sq] float32")
+    _check(_lib.r3d_attn_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                     _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                                     float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd_noalloc")
     return (out, lse) if lse is not None else out
 
 

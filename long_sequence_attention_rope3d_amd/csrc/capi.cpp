@@ -245,6 +245,31 @@ int device_cus() {
   return n;
 }
 
+// Device scratch of r3d_attn_fwd_noalloc, for callers that cannot allocate:
+// one fixed array per GPU, held until the process ends.  Host code never
+// uses the name itself (on the host it is a stand-in, not a device
+// address): scratch_ptr() returns the array's address on the current device,
+// taken with hipGetSymbolAddress once per device.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Address of `scratch` on the current device (NULL and *err set on failure).
+void* scratch_ptr(hipError_t* err) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) return it->second;
+  void* p = nullptr;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !p) return nullptr;
+  addr[dev] = p;
+  return p;
+}
+
 constexpr int64_t kWsAlign = 256;  // each workspace region starts on a 256-byte boundary
 int64_t ws_round(int64_t bytes) { return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
@@ -325,15 +350,34 @@ int64_t constmax_flags_ints(int64_t B, int64_t H, int64_t Sq) {
 
 // Shared by both output layouts: the validation is identical (out has the
 // same number of elements either way).
+// scratch_limit >= 0: the call of r3d_attn_fwd_noalloc, whose workspace is
+// the fixed scratch array of that many bytes (a key split whose partials do
+// not fit runs unsplit; statistics that do not fit are rejected).
 int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
                   int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk, int32_t dtype,
-                  void* workspace, size_t workspace_bytes, bool out_bshd, void* stream) {
+                  void* workspace, size_t workspace_bytes, bool out_bshd, void* stream,
+                  int64_t scratch_limit = -1) {
+  const char* what = scratch_limit >= 0 ? "attn_fwd_noalloc" : "attn_fwd";
   int64_t nq, nk, bhq;
-  int st = check_attn_args("attn_fwd", q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
+  int st = check_attn_args(what, q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
   if (st != R3D_OK) return st;
-  if (kv_chunk < 0) return fail(R3D_EINVAL, "attn_fwd: kv_chunk=%lld < 0", (long long)kv_chunk);
-  const AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, out_bshd);
-  st = check_workspace("attn_fwd", workspace, workspace_bytes, plan.total(), q, k, v, out, lse, nq, nk, bhq,
+  if (kv_chunk < 0) return fail(R3D_EINVAL, "%s: kv_chunk=%lld < 0", what, (long long)kv_chunk);
+  AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, out_bshd);
+  if (scratch_limit >= 0 && plan.total() > 0) {
+    if (plan.stats_bytes > scratch_limit)
+      return fail(R3D_EINVAL, "%s: B*H=%lld needs %lld bytes of scratch, more than the %lld available", what,
+                  (long long)(B * H), (long long)plan.stats_bytes, (long long)scratch_limit);
+    if (plan.total() > scratch_limit) {  // partials do not fit: no key split
+      plan.n_split = 1;
+      plan.split_len = Skv;
+      plan.parts_bytes = 0;
+    }
+    hipError_t e = hipSuccess;
+    workspace = scratch_ptr(&e);
+    if (!workspace) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e, what);
+    workspace_bytes = (size_t)scratch_limit;
+  }
+  st = check_workspace(what, workspace, workspace_bytes, plan.total(), q, k, v, out, lse, nq, nk, bhq,
                        elt_size(dtype));
   if (st != R3D_OK) return st;
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
@@ -357,7 +401,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   } else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
                              D, scale, chunk, out_bshd, strm);
-  return hip_status(e, "attn_fwd");
+  return hip_status(e, what);
 }
 
 int ws_size_out(const char* what, int64_t need, size_t* bytes) {
@@ -396,6 +440,13 @@ R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
                          int64_t kv_chunk, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, workspace, workspace_bytes,
                        false, stream);
+}
+
+R3D_API int r3d_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                                 int64_t kv_chunk, int32_t dtype, void* stream) {
+  return attn_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, dtype, nullptr, 0, false, stream,
+                       kScratchBytes);
 }
 
 R3D_API int r3d_attn_fwd_bshd(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -30,7 +30,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute",
                                   "r3d_joint_concat_permute_qknorm", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
-                                  "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
+                                  "r3d_attn_fwd_noalloc", "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
                                   "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge", "r3d_last_error",
                                   "r3d_version"])
 
@@ -60,6 +60,7 @@ F = ctypes.c_float
 SZ = ctypes.c_size_t
 LIB.r3d_attn_fwd.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P, SZ, P]
 LIB.r3d_attn_fwd_bshd.argtypes = LIB.r3d_attn_fwd.argtypes
+LIB.r3d_attn_fwd_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I64, I32, P]
 LIB.r3d_attn_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
 LIB.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, F, I32, P, SZ, P]
 LIB.r3d_attn_fwd_constmax_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
@@ -145,6 +146,22 @@ def test_attn_fwd_rejects_bad_workspace(fn):
     assert _attn(fn, ws=L_ - 64) == -1 and "workspace overlaps" in LIB.r3d_last_error().decode()
     # argument errors are reported before workspace errors
     assert _attn(fn, ws=None, D=96) == -2
+
+
+def test_attn_fwd_noalloc_rejects():
+    def call(**kw):
+        a = dict(q=A, k=B_, v=C, out=O, lse=L_, B=1, H=2, Sq=64, Skv=64, D=128, kv_chunk=0, dtype=1)
+        a.update(kw)
+        return LIB.r3d_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Sq"],
+                                        a["Skv"], a["D"], 0.125, a["kv_chunk"], a["dtype"], None)
+    # the fixed scratch holds the statistics of at most 32768 heads (512 bytes each)
+    assert call(B=2, H=16385, Sq=1, Skv=1) == -1
+    msg = LIB.r3d_last_error().decode()
+    assert "attn_fwd_noalloc" in msg and "scratch" in msg and "16777216" in msg
+    assert call(D=96) == -2
+    assert call(q=None) == -1 and "NULL" in LIB.r3d_last_error().decode()
+    assert call(out=A) == -1 and "overlaps" in LIB.r3d_last_error().decode()
+    assert call(kv_chunk=-2) == -1
 
 
 def test_attn_fwd_constmax_rejects():
