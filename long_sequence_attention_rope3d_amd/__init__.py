@@ -39,7 +39,9 @@ __all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspa
            "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "lib", "librope3d_attn.so")
+# R3D_LIBRARY names another build of the same library (the host-sanitizer
+# build of tests/sanitize.py); by default the in-tree one.
+_LIB_PATH = os.environ.get("R3D_LIBRARY") or os.path.join(_PKG, "lib", "librope3d_attn.so")
 
 R3D_OK, R3D_EINVAL, R3D_EUNSUPPORTED, R3D_EHIP = 0, -1, -2, -3
 _F32, _BF16 = 0, 1

@@ -30,6 +30,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+# R3D_ORACLE_LIBRARY names another build of oracle.c (the host-sanitizer
+# build of tests/sanitize.py), used as is; by default liboracle.so here.
+_LIB_OVERRIDE = os.environ.get("R3D_ORACLE_LIBRARY")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 _lib = None
@@ -51,9 +54,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I = ctypes.c_int
