@@ -13,8 +13,15 @@ is already resident in HBM:
 attn_fwd).  `value` is attention TFLOP/s over the whole step, counting
 4*B*H*Sq*Skv*D flops per step.  The standalone rope3d_apply and lse_merge
 entry points are timed after the step loop on the same workload shapes and
-reported under "kernels", with the shard-shape proxies and attn_fwd on the
-long-video workload (GPU-drawn inputs with its outlier keys).
+reported under "kernels", with the shard-shape proxies, attn_fwd on the
+lite-clip and image-dit workloads (their own seeded inputs and kv_chunk) and
+on the long-video workload (GPU-drawn inputs with its outlier keys).
+
+roofline.achieved is 4*B*H*Sq*Skv*D over the mean duration of the timed
+r3d_attn_fwd calls, measured with HIP events on the launch stream; a call is
+two dispatches, the head-statistics pre-pass (reads K and V once) and the
+attention kernel, so the call time is a slight over-estimate of the attention
+kernel's own.
 
 Prints ONE JSON line.
 """
@@ -188,13 +195,17 @@ def main():
     kernels = {}
     if not args.no_kernels:
         kernels = time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream)
-        if w.name == "pro-clip" and not args.no_long_video:
-            kernels["attn_fwd_long_video"] = time_long_video(torch, r3d, dev, stream)
+        if w.name == "pro-clip":
+            for other in ("lite-clip", "image-dit"):
+                kernels["attn_fwd_" + other.replace("-", "_")] = time_attn_workload(torch, r3d, other, dev, stream)
+            if not args.no_long_video:
+                kernels["attn_fwd_long_video"] = time_long_video(torch, r3d, dev, stream)
 
     traffic_bytes = _traffic_for_current_kernel()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_bytes, "kernel": "attn_fwd (attn_bf16_kernel<128>)",
+                "traffic": traffic_bytes,
+                "kernel": "r3d_attn_fwd call (head_stats_kernel<128> + attn_bf16_kernel<128>)",
                 "counters": _mfma_counters_for_current_kernel()}
 
     cpu = None
@@ -326,6 +337,40 @@ def time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream, reps
         for kname in ("attn_fwd_ulysses_shard", "attn_fwd_cp_shard"):
             log(f"{kname}: {res[kname]['ms']:.3f} ms, {res[kname]['TFLOPs']:.1f} TFLOP/s")
     return res
+
+
+def time_attn_workload(torch, r3d, name, dev, stream, reps: int = 20):
+    """attn_fwd alone on another workload's full shape (its seeded host inputs, RoPE and
+    re-layout by joint_concat_permute, its kv_chunk): median and min ms per call over
+    `reps` calls each bracketed by HIP events, TFLOP/s and fraction of the bf16 peak."""
+    from workloads import by_name, make_inputs
+    w = by_name(name)
+    inp = make_inputs(w)
+    rope = r3d.Rope3D(w.grid, w.split, w.theta)
+    q = r3d.joint_concat_permute([s.to(dev) for s in inp["q"]], rope)
+    k = r3d.joint_concat_permute([s.to(dev) for s in inp["k"]], rope)
+    v = r3d.joint_concat_permute([s.to(dev) for s in inp["v"]], None)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, r3d.attn_fwd_workspace_size(w.B, w.H, w.S, w.S, w.D, w.kv_chunk, q.dtype)),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: r3d.attn_fwd(q, k, v, scale=w.scale, kv_chunk=w.kv_chunk, out=out, lse=lse,  # noqa: E731
+                                workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    tf = w.attn_flops / (med * 1e-3) / 1e12
+    log(f"attn_fwd_{w.name}: {med:.4f} ms (min {ms[0]:.4f}), {tf:.1f} TFLOP/s")
+    return {"ms": round(med, 4), "ms_min": round(ms[0], 4), "S": w.S, "H": w.H, "kv_chunk": w.kv_chunk,
+            "TFLOPs": round(tf, 2), "frac_bf16_peak": round(tf / MI355X_BF16_PEAK_TFLOPS, 4)}
 
 
 def time_long_video(torch, r3d, dev, stream, reps: int = 3):

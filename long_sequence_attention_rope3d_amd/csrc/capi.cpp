@@ -131,7 +131,7 @@ R3D_API int r3d_rope3d_apply(const void* x, void* y, int32_t dtype, int64_t B, i
   if (!product(n, {B, Nv, H, D}) || n > kMaxElems) return fail(R3D_EINVAL, "rope3d_apply: tensor too large");
   if (x != y && overlap(x, n * es, y, n * es))
     return fail(R3D_EINVAL, "rope3d_apply: x and y overlap without being identical");
-  if (!launch_fits(((Nv + r3d::kPermuteTokRope - 1) / r3d::kPermuteTokRope) * B, r3d::kPermuteThreadsRope))
+  if (!launch_fits(((Nv + r3d::kRopeApplyTok - 1) / r3d::kRopeApplyTok) * B, r3d::kRopeApplyThreads))
     return fail(R3D_EINVAL, "rope3d_apply: B*Nv too large for one launch");
   r3d::RopeArgs ra{};
   int st = build_rope(rope, D, Nv, ra);

@@ -18,12 +18,15 @@ constexpr int kMaxPairs = 64;  // D/2 for D = 128
 
 // rope_permute launches, per path (the host's launch-size checks use these):
 // plain copy, blocks of kPermuteThreads threads over kPermuteTok consecutive
-// tokens; with RoPE, kPermuteThreadsRope over kPermuteTokRope; with the
+// tokens; the re-layout with RoPE, kPermuteThreadsRope over kPermuteTokRope;
+// rope3d_apply (no re-layout), kRopeApplyThreads over kRopeApplyTok; with the
 // QK-norm, kPermuteThreadsNorm over kPermuteTokNorm.
 constexpr int kPermuteThreads = 512;
 constexpr int kPermuteTok = 4;
 constexpr int kPermuteThreadsRope = 256;
-constexpr int kPermuteTokRope = 2;
+constexpr int kPermuteTokRope = 4;
+constexpr int kRopeApplyThreads = 256;
+constexpr int kRopeApplyTok = 2;
 constexpr int kPermuteThreadsNorm = 256;
 constexpr int kPermuteTokNorm = 4;
 

@@ -42,13 +42,13 @@ namespace {
 // chunks (3 for 24 heads of 128 bf16) and many blocks are in flight:
 // measured 12% faster than 256-thread blocks of 8 tokens whose threads
 // walked 12 heads each (a plain 16-byte-per-thread copy of the same bytes
-// peaks at about 6.5 TB/s on the MI355X).  With RoPE, 256-thread blocks of
-// 2 tokens (again 3 chunks per thread): 3% faster than the copy's shape,
-// each block's cos/sin table then being a single round of sincos.
+// peaks at about 6.5 TB/s on the MI355X).  The re-layout with RoPE:
+// 256-thread blocks of 4 tokens, 6 chunks per thread all loaded before the
+// cos/sin table is formed (111.0 vs 116.4 us for 2 tokens and 3 chunks at
+// 52k, bit-identical); rope3d_apply keeps 2 tokens and 3 chunks per thread
+// (102 vs 106 us the other way round).
 constexpr int kThreads = kPermuteThreads;
 constexpr int kTok = kPermuteTok;
-constexpr int kThreadsRope = kPermuteThreadsRope;
-constexpr int kTokRope = kPermuteTokRope;
 // With the QK-norm a block is 256 threads over 4 tokens, so that each thread
 // holds only a few of its token's chunks (kHold) through the norm's
 // reduction: the kernel then fits 6 waves per SIMD instead of 4, and the
@@ -191,16 +191,23 @@ __device__ __forceinline__ double chunk_sumsq(u32x4 v) {
 // NORM (with PERMUTE, D in {64, 128}): segments with a weight vector get the
 // RMS QK-norm before the rotation.
 // Block shape of each path: tokens per block and threads per block.
-template <bool ROPE, bool NORM>
-constexpr int tok_per_block() { return NORM ? kTokNorm : ROPE ? kTokRope : kTok; }
-template <bool ROPE, bool NORM>
-constexpr int threads_per_block() { return NORM ? kThreadsNorm : ROPE ? kThreadsRope : kThreads; }
+template <bool PERMUTE, bool ROPE, bool NORM>
+constexpr int tok_per_block() {
+  return NORM ? kTokNorm : !PERMUTE ? kRopeApplyTok : ROPE ? kPermuteTokRope : kTok;
+}
+template <bool PERMUTE, bool ROPE, bool NORM>
+constexpr int threads_per_block() {
+  return NORM ? kThreadsNorm : !PERMUTE ? kRopeApplyThreads : ROPE ? kPermuteThreadsRope : kThreads;
+}
+// 16-byte chunks each thread loads up front and keeps in registers.
+template <bool PERMUTE, bool ROPE, bool NORM>
+constexpr int chunks_held() { return (NORM || (PERMUTE && ROPE)) ? 6 : 3; }
 
 template <bool BF16, bool PERMUTE, bool ROPE, bool NORM>
-__global__ __launch_bounds__((threads_per_block<ROPE, NORM>())) void rope_permute_kernel(
+__global__ __launch_bounds__((threads_per_block<PERMUTE, ROPE, NORM>())) void rope_permute_kernel(
     SegArgs segs, void* out, int H, int D, int64_t n_tb, RopeArgs rope) {
-  constexpr int kT = tok_per_block<ROPE, NORM>();       // tokens per block
-  constexpr int kNT = threads_per_block<ROPE, NORM>();  // threads per block
+  constexpr int kT = tok_per_block<PERMUTE, ROPE, NORM>();       // tokens per block
+  constexpr int kNT = threads_per_block<PERMUTE, ROPE, NORM>();  // threads per block
   __shared__ double2 cs[kT][kMaxPairs];
   // Norm partial sums, one per (head group, token): hstep * kT = kNT / cpr
   // of them, and cpr >= 8 for the row widths the norm accepts.
@@ -275,7 +282,7 @@ __global__ __launch_bounds__((threads_per_block<ROPE, NORM>())) void rope_permut
     // head H-1 of the same token, in bounds, and is not used): with a branch
     // around them the compiler copied the loaded registers at the join, i.e.
     // waited for the loads before the table below.
-    constexpr int kHold = NORM ? 6 : 3;  // all of them for bf16, D = 128, H <= 24
+    constexpr int kHold = chunks_held<PERMUTE, ROPE, NORM>();  // all of them for bf16, D = 128, H <= 24
     u32x4 held[kHold];
     const int nh = (valid && H > h0) ? (H - h0 + hstep - 1) / hstep : 0;  // this thread's heads
     auto ld = [&](int h) {
@@ -388,8 +395,8 @@ __global__ __launch_bounds__((threads_per_block<ROPE, NORM>())) void rope_permut
 template <bool PERMUTE, bool ROPE, bool NORM = false>
 hipError_t launch_typed(bool bf16, const SegArgs& segs, void* out, int64_t B, int64_t H, int64_t D,
                         const RopeArgs& rope, hipStream_t stream) {
-  constexpr int kT = tok_per_block<ROPE, NORM>();
-  constexpr int kNT = threads_per_block<ROPE, NORM>();
+  constexpr int kT = tok_per_block<PERMUTE, ROPE, NORM>();
+  constexpr int kNT = threads_per_block<PERMUTE, ROPE, NORM>();
   const int64_t n_tb = (segs.S + kT - 1) / kT;  // token blocks per batch row
   const unsigned grid = (unsigned)(n_tb * B);
   if (bf16)
