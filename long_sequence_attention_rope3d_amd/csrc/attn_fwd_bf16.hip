@@ -20,11 +20,12 @@
 //     (§Memory and Compute Benefits: the split keeps full attention quality).
 // The softmax runs in the log2 domain: logits are multiplied by
 // c = |scale| * log2(e) inside one FMA, so p = 2^(s*c - m).
-// A launch whose query tiles leave the CUs mostly idle can also split each
-// tile's keys into ranges of whole chunks run by separate blocks; each then
-// writes its fp32 partial (O, lse) and the ranges are combined by the same
-// log-sum-exp merge in a second kernel (lse_merge.hip) -- ring attention's
-// per-shard partials, with the shards as blocks of one launch.
+// A launch whose last round of blocks would leave many CUs idle can also
+// split the keys of that round's query tiles into ranges of whole chunks run
+// by separate blocks; each then writes its fp32 partial (O, lse) and the
+// ranges are combined by the same log-sum-exp merge in a second kernel
+// (lse_merge.hip) -- ring attention's per-shard partials, with the shards as
+// blocks of one launch.
 //
 // Mapping onto CDNA4
 // ------------------
@@ -34,10 +35,11 @@
 //   wave at 168 registers (the kernel needs 162 and spills nothing).  384
 //   also divides the 52608-token workload exactly, and 137 query tiles per
 //   head keep the last round of blocks on the CUs nearly full.
-// * Grid = B*H*n_split*ceil(Sq/384) blocks, re-numbered so consecutive query
-//   tiles of one (head, key range) land on the same XCD (hardware hands block
-//   i to XCD i % 8): the CUs of an XCD stream the same K/V and share it in
-//   that XCD's L2.
+// * Grid = one block per query tile (B*H*ceil(Sq/384) tiles), plus n_split
+//   blocks per tile of a split last round in place of one; re-numbered so
+//   consecutive query tiles over the same keys land on the same XCD
+//   (hardware hands block i to XCD i % 8): the CUs of an XCD stream the same
+//   K/V and share it in that XCD's L2.
 // * K/V tiles of kBN = 128 keys are copied global -> LDS by DMA
 //   (global_load_lds_dwordx4) into two stage buffers, row-major [key][d],
 //   with the 16-byte chunks of every row XOR-swizzled so that the operand
@@ -307,9 +309,9 @@ template <int D, bool kConstMax>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
-    uint32_t qsign, int64_t chunk, int n_qt, int n_blocks, int out_bshd, const float* __restrict__ stats,
-    int n_split, int64_t split_len, int out_f32, int chunk_bits, int* __restrict__ flags_out,
-    const int* __restrict__ fix_flags) {
+    uint32_t qsign, int64_t chunk, int n_qt, int n_tiles, int n_bulk, int out_bshd, const float* __restrict__ stats,
+    int n_split, int64_t split_len, float* __restrict__ o_parts, float* __restrict__ l_parts, int64_t tail_row0,
+    int chunk_bits, int* __restrict__ flags_out, const int* __restrict__ fix_flags) {
   using G = Geom<D>;
   // K/V stage buffers (the third only with kStages == 3).
   // K/V stage buffers in one array, K stages first: [K_0 .. K_{kStages-1} | V_0 .. V_{kStages-1}].
@@ -321,23 +323,31 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStages * G::kTile];
   static_assert((kStages - 1) * G::kTile * 2 + kBN * G::kCpr * 16 <= 65536, "K reads within the DS offset");
 
-  // Block -> (head, key split, query tile): XCD x runs logical tiles
-  // [x*per + min(x, rem), ...), and consecutive logical tiles are consecutive
-  // query tiles of one (head, split), which stream the same keys.
+  // Block -> work.  Query tiles are numbered head-major (logical tile =
+  // bh * n_qt + qt).  Blocks [0, n_bulk) run tiles [0, n_bulk) over all keys;
+  // the blocks after them run each remaining tile n_split times, once per
+  // key range (split), as pieces whose fp32 partials an lse_merge combines.
+  // Within each group, XCD x runs indices [x*per + min(x, rem), ...), so that
+  // consecutive indices -- consecutive query tiles over the same keys -- share
+  // an XCD's L2 (hardware hands block i to XCD i % 8).
   const int bid = blockIdx.x;
-  const int per = n_blocks / kXcds, rem = n_blocks % kXcds;
-  const int xcd = bid % kXcds, slot = bid / kXcds;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int hs = logical / n_qt;  // head * n_split + split
-  const int qt = logical - hs * n_qt;
-  const int64_t bh = hs / n_split;
-  const int split = hs - (int)bh * n_split;
-  // This block's keys: [kv_begin, kv_end), a whole number of chunks (or, with
-  // one chunk, of tiles); n_split = 1 is the whole sequence.
+  const bool piece = bid >= n_bulk;
+  const int n_tail = n_tiles - n_bulk;
+  const int nb = piece ? n_tail * n_split : n_bulk;
+  const int b0 = piece ? bid - n_bulk : bid;
+  const int per = nb / kXcds, rem = nb % kXcds;
+  const int xcd = b0 % kXcds, slot = b0 / kXcds;
+  const int idx = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int split = piece ? idx / n_tail : -1;
+  const int logical = piece ? n_bulk + (idx - split * n_tail) : idx;
+  const int64_t bh = logical / n_qt;
+  const int qt = logical - (int)bh * n_qt;
+  // This block's keys: [kv_begin, kv_end), the whole sequence or one range
+  // of split_len keys (a whole number of chunks, or with one chunk of tiles).
   const int skv = (int)Skv;
   const int chunk32 = (int)(chunk < Skv ? chunk : Skv);
-  const int kv_begin = split * (int)split_len;
-  const int kv_end = (skv - kv_begin > (int)split_len) ? kv_begin + (int)split_len : skv;
+  const int kv_begin = piece ? split * (int)split_len : 0;
+  const int kv_end = (piece && skv - kv_begin > (int)split_len) ? kv_begin + (int)split_len : skv;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -406,7 +416,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   {
     static_assert(kStatParts == 64, "one partial per lane");
     float a = stats[bh * kStatParts + lane];
-    float b = stats[((int64_t)(n_blocks / (n_split * n_qt)) + bh) * kStatParts + lane];
+    float b = stats[((int64_t)(n_tiles / n_qt) + bh) * kStatParts + lane];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       a = fmaxf(a, __shfl_xor(a, o));
@@ -642,7 +652,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
       flags_out[(int64_t)logical * kWaves + wave] = any_bad ? 1 : 0;
   }
 
-  // ---- epilogue: out (bf16, RNE; or fp32 for a key-split partial) and lse (natural log) ----
+  // ---- epilogue: out (bf16, RNE; or an fp32 partial for a piece) and lse (natural log) ----
   // The last tile closed a chunk, so acc = O and m = L (log2).
   // oacc[b][i] of lane (r32, hf) is d = 32*b + 8*(i/4) + 4*hf + i%4 of query qrow.
   // The lane's row and half are formed again here from the hardware lane
@@ -653,20 +663,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   const int e_hf = e_lane >> 5;
   const int e_qrow = qt * kBM + wave * 32 + (e_lane & 31);
   if (e_qrow < sq) {
-    // Row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major); a
-    // split partial goes to [n_split, B*H*Sq, D] (lse [n_split, B*H*Sq]).
-    const int64_t b = bh / H;
-    const int64_t nbh = (int64_t)n_blocks / ((int64_t)n_split * n_qt);  // B*H
-    const int64_t prow = ((int64_t)split * nbh + bh) * Sq + e_qrow;
-    if (out_f32) {
-      float* op = static_cast<float*>(out) + prow * D;
+    if (piece) {
+      // Partial of a piece: [n_split, rows, D] and lse [n_split, rows], rows
+      // counted from the first row of the split tiles (tail_row0 of [B*H*Sq]).
+      const int64_t n_rows = (int64_t)(n_tiles / n_qt) * Sq - tail_row0;
+      const int64_t prow = (int64_t)split * n_rows + (bh * Sq + e_qrow - tail_row0);
+      float* op = o_parts + prow * D;
 #pragma unroll
       for (int b = 0; b < G::kDBlk; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *reinterpret_cast<float4*>(op + 32 * b + 8 * g + 4 * e_hf) =
               make_float4(oacc[b][4 * g], oacc[b][4 * g + 1], oacc[b][4 * g + 2], oacc[b][4 * g + 3]);
+      if (e_hf == 0) l_parts[prow] = m_run * 0.69314718055994530942f;
     } else {
+      // Row of (b, h, qrow): [B, H, Sq, D], or [B, Sq, H, D] (token-major).
+      const int64_t b = bh / H;
+      const int64_t prow = bh * Sq + e_qrow;
       const int64_t orow = out_bshd ? (b * Sq + e_qrow) * H + (bh - b * H) : prow;
       uint16_t* op = static_cast<uint16_t*>(out) + orow * D;
 #pragma unroll
@@ -677,8 +690,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
                                 pack_bf16(oacc[b][4 * g + 2], oacc[b][4 * g + 3])};
           *reinterpret_cast<u32x2*>(op + 32 * b + 8 * g + 4 * e_hf) = w;
         }
+      if (lse && e_hf == 0) lse[prow] = m_run * 0.69314718055994530942f;
     }
-    if (lse && e_hf == 0) lse[prow] = m_run * 0.69314718055994530942f;
   }
 }
 
@@ -757,25 +770,32 @@ hipError_t launch_head_stats(const uint16_t* kp, const uint16_t* vp, float* stat
 template <bool kConstMax>
 hipError_t launch_attn_kernel(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
                               int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                              bool out_bshd, const float* stats, int n_split, int64_t split_len, bool out_f32,
-                              int* flags_out, const int* fix_flags, hipStream_t stream) {
+                              bool out_bshd, const float* stats, const KeySplit& ks, float* o_parts,
+                              float* l_parts, int* flags_out, const int* fix_flags, hipStream_t stream) {
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
-  const int n_blocks = (int)(B * H * n_split * n_qt);
+  const int n_tiles = (int)(B * H * n_qt);
+  const int n_split = ks.n_split > 1 ? ks.n_split : 1;
+  const int n_bulk = n_split > 1 ? (int)ks.n_bulk : n_tiles;
+  const int n_blocks = n_bulk + (n_tiles - n_bulk) * n_split;
+  const int64_t tail_row0 = attn_bf16_split_first_row(n_bulk, Sq);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  // Longest run of keys accumulated without a merge: a chunk, within a split.
-  const int chunk_bits = bits_for(std::min(std::min(kv_chunk, Skv), n_split > 1 ? split_len : Skv));
+  // Longest run of keys accumulated without a merge: a chunk (within a key
+  // range when every tile is split).
+  int64_t run = std::min(kv_chunk, Skv);
+  if (n_split > 1 && n_bulk == 0) run = std::min(run, ks.split_len);
+  const int chunk_bits = bits_for(run);
   const auto* qp = static_cast<const uint16_t*>(q);
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
   if (D == 64)
     attn_bf16_kernel<64, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, stats, n_split,
-        split_len, out_f32 ? 1 : 0, chunk_bits, flags_out, fix_flags);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_tiles, n_bulk, out_bshd ? 1 : 0, stats,
+        n_split, ks.split_len, o_parts, l_parts, tail_row0, chunk_bits, flags_out, fix_flags);
   else
     attn_bf16_kernel<128, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
-        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_blocks, out_bshd ? 1 : 0, stats, n_split,
-        split_len, out_f32 ? 1 : 0, chunk_bits, flags_out, fix_flags);
+        qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_tiles, n_bulk, out_bshd ? 1 : 0, stats,
+        n_split, ks.split_len, o_parts, l_parts, tail_row0, chunk_bits, flags_out, fix_flags);
   return hipGetLastError();
 }
 
@@ -789,41 +809,57 @@ bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq) {
   return fits(nbh * kStatParts, kNormThreads) && fits(nbh * ((Sq + kBM - 1) / kBM), kThreads);
 }
 
-int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
-                        int64_t* split_len) {
-  *split_len = Skv;
+int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq) {
   const int64_t n_qt = (Sq + kBM - 1) / kBM;
-  const int64_t blocks = B * H * n_qt;
-  if (n_cus <= 0 || blocks >= 4 * (int64_t)n_cus) return 1;  // the last round is a small share already
-  // Split only a grid that leaves the CUs mostly idle: under an eighth of
-  // them, or a last round at most a quarter full.  (Measured: a last round
-  // filled 55-70% costs less than its share -- the chip is power-limited and
-  // clocks up when fewer CUs run -- and splitting such grids was 1-10% slower
-  // or no faster, while the merge adds traffic.)
-  const int64_t last = blocks % n_cus;
-  if (!(blocks * 8 < n_cus || (last != 0 && last * 4 <= n_cus))) return 1;
-  // Split unit: a chunk when there are several, else a tile; at least 1024 keys per split.
-  const int64_t unit = kv_chunk < Skv ? kv_chunk : kBN;
-  const int64_t n_units = (Skv + unit - 1) / unit;
-  auto eff = [&](int64_t nb) {  // busy share of the CU rounds that nb equal blocks take
-    const int64_t rounds = (nb + n_cus - 1) / n_cus;
-    return (double)nb / (double)(rounds * n_cus);
+  return (n_bulk / n_qt) * Sq + (n_bulk % n_qt) * kBM;
+}
+
+KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                             int n_cus) {
+  const int64_t n_qt = (Sq + kBM - 1) / kBM;
+  const int64_t tiles = B * H * n_qt;
+  KeySplit none;
+  none.n_bulk = tiles;
+  none.n_split = 1;
+  none.split_len = Skv;
+  if (n_cus <= 0) return none;
+  const int64_t tail = tiles % n_cus;  // tiles of the last, partly filled round
+  if (tail == 0) return none;
+  const int64_t full = tiles / n_cus;
+  // Cost model, in units of one tile over all Skv keys on a fully busy chip,
+  // fitted to timings of forced splits on the MI355X (shard shapes, image and
+  // long-video workloads).  A round that fills a share f of the CUs costs
+  // 0.83 + 0.17 f of a full one: the chip is power-limited and clocks up when
+  // fewer CUs run, but not by much.  A piece of len keys costs like len + 700
+  // keys (prologue, pipeline fill, partial write); the partials' write and
+  // merge stream at ~5 TB/s.
+  auto round_cost = [](double f) { return 0.83 + 0.17 * f; };
+  auto rounds = [&](int64_t nb, double len) {  // nb blocks of relative length len
+    const int64_t r = nb / n_cus, f = nb % n_cus;
+    return len * ((double)r + (f ? round_cost((double)f / n_cus) : 0.0));
   };
-  int best = 1;
-  int64_t best_len = Skv;
-  double best_eff = eff(blocks);
+  const double base = (double)full + round_cost((double)tail / n_cus);
+  // Seconds of one tile at the kernel's rate (~1250 TFLOP/s over the chip).
+  const double tile_s = 4.0 * kBM * (double)Skv * (double)D / (1250e12 / n_cus);
+  const double tail_rows = (double)(B * H * Sq - attn_bf16_split_first_row(tiles - tail, Sq));
+  const int64_t unit = kv_chunk < Skv ? kv_chunk : kBN;  // ranges hold whole chunks, else whole tiles
+  const int64_t n_units = (Skv + unit - 1) / unit;
+  KeySplit best = none;
+  double best_cost = base;
   for (int s = 2; s <= kMaxKeySplit; ++s) {
     const int64_t len = ((n_units + s - 1) / s) * unit;
-    if (len < 1024) break;
-    const int64_t n = (Skv + len - 1) / len;  // splits actually made
-    const double e = eff(blocks * n);
-    if (e > best_eff + 0.05) {
-      best = (int)n;
-      best_len = len;
-      best_eff = e;
+    if (len < kMinSplitKeys) break;
+    const int64_t n = (Skv + len - 1) / len;  // ranges actually made
+    if (n < 2) continue;
+    const double merge_s = ((double)n * tail_rows * (D + 1) * 4.0 * 2.0 + tail_rows * D * 2.0) / 5e12 + 10e-6;
+    const double cost = (double)full + rounds(tail * n, (double)(len + 700) / (double)Skv) + merge_s / tile_s;
+    if (cost < base * 0.98 && cost < best_cost) {  // a split must gain 2%
+      best.n_bulk = tiles - tail;
+      best.n_split = (int)n;
+      best.split_len = len;
+      best_cost = cost;
     }
   }
-  *split_len = best_len;
   return best;
 }
 
@@ -833,13 +869,18 @@ int attn_bf16_waves() { return kWaves; }
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse, float* stats,
                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
-                            int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len, bool out_f32,
+                            int64_t kv_chunk, bool out_bshd, const KeySplit& ks, float* o_parts, float* l_parts,
                             hipStream_t stream) {
   hipError_t e = launch_head_stats(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), stats, B, H,
                                    Skv, D, stream);
   if (e != hipSuccess) return e;
-  return launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, stats, n_split,
-                                   split_len, out_f32, nullptr, nullptr, stream);
+  e = launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, stats, ks, o_parts,
+                                l_parts, nullptr, nullptr, stream);
+  if (e != hipSuccess || ks.n_split <= 1) return e;
+  // Merge the pieces' partials into the rows of the split tiles.
+  const int64_t row0 = attn_bf16_split_first_row(ks.n_bulk, Sq);
+  return launch_lse_merge(o_parts, l_parts, ks.n_split, false, static_cast<uint16_t*>(out) + row0 * D,
+                          lse ? lse + row0 : nullptr, true, B * H * Sq - row0, D, stream);
 }
 
 hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -848,13 +889,17 @@ hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v
   hipError_t e = launch_head_stats(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), stats, B, H,
                                    Skv, D, stream);
   if (e != hipSuccess) return e;
-  e = launch_attn_kernel<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, 1, Skv, false, flags,
-                               nullptr, stream);
+  KeySplit whole;
+  whole.n_bulk = B * H * ((Sq + kBM - 1) / kBM);
+  whole.n_split = 1;
+  whole.split_len = Skv;
+  e = launch_attn_kernel<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, whole, nullptr,
+                               nullptr, flags, nullptr, stream);
   if (e != hipSuccess) return e;
   // Recompute the flagged tiles with the online reference (one chunk: the
   // same function; blocks of clean tiles return at once).
-  return launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, 1, Skv, false,
-                                   nullptr, flags, stream);
+  return launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, whole, nullptr,
+                                   nullptr, nullptr, flags, stream);
 }
 
 }  // namespace r3d

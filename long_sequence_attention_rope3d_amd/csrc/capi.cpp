@@ -324,23 +324,32 @@ int check_workspace(const char* what, const void* ws, size_t ws_bytes, int64_t n
 }
 
 // Workspace plan of a bf16 attn_fwd call: the head statistics, then (for a
-// key-split launch) the fp32 partials n_split x rows x (D + 1).
+// key-split launch) the fp32 partials n_split x rows x (D + 1) of the split
+// tiles' rows.
 struct AttnPlan {
-  int n_split = 1;
-  int64_t split_len = 0;
-  int64_t stats_bytes = 0, parts_bytes = 0;
+  r3d::KeySplit ks;
+  int64_t stats_bytes = 0, parts_bytes = 0, part_rows = 0;
   int64_t total() const { return stats_bytes + parts_bytes; }
+  void unsplit(int64_t B, int64_t H, int64_t Sq, int64_t Skv) {
+    ks.n_bulk = B * H * r3d::attn_bf16_query_tiles(Sq);
+    ks.n_split = 1;
+    ks.split_len = Skv;
+    parts_bytes = part_rows = 0;
+  }
 };
 
 AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype,
                    bool out_bshd) {
   AttnPlan p;
-  p.split_len = Skv;
+  p.unsplit(B, H, Sq, Skv);
   if (dtype != R3D_BF16) return p;  // the fp32 kernel needs no workspace
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
-  if (!out_bshd) p.n_split = r3d::attn_bf16_key_split(B, H, Sq, Skv, chunk, device_cus(), &p.split_len);
-  if (p.n_split > 1) p.parts_bytes = ws_round(p.n_split * B * H * Sq * (D + 1) * 4);
+  if (!out_bshd) p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
+  if (p.ks.n_split > 1) {
+    p.part_rows = B * H * Sq - r3d::attn_bf16_split_first_row(p.ks.n_bulk, Sq);
+    p.parts_bytes = ws_round(p.ks.n_split * p.part_rows * (D + 1) * 4);
+  }
   return p;
 }
 
@@ -367,11 +376,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
     if (plan.stats_bytes > scratch_limit)
       return fail(R3D_EINVAL, "%s: B*H=%lld needs %lld bytes of scratch, more than the %lld available", what,
                   (long long)(B * H), (long long)plan.stats_bytes, (long long)scratch_limit);
-    if (plan.total() > scratch_limit) {  // partials do not fit: no key split
-      plan.n_split = 1;
-      plan.split_len = Skv;
-      plan.parts_bytes = 0;
-    }
+    if (plan.total() > scratch_limit) plan.unsplit(B, H, Sq, Skv);  // partials do not fit: no key split
     hipError_t e = hipSuccess;
     workspace = scratch_ptr(&e);
     if (!workspace) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e, what);
@@ -385,19 +390,16 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   hipError_t e;
   if (dtype == R3D_BF16) {
     float* stats = static_cast<float*>(workspace);
-    if (plan.n_split > 1) {
-      // Few query tiles (a shard's shape): the keys are split over several
-      // blocks per tile, and the fp32 partials merged.
-      float* o_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.stats_bytes);
-      float* l_parts = o_parts + plan.n_split * bhq * D;
-      e = r3d::launch_attn_bf16(q, k, v, o_parts, l_parts, stats, B, H, Sq, Skv, D, scale, chunk, false,
-                                plan.n_split, plan.split_len, true, strm);
-      if (e == hipSuccess)
-        e = r3d::launch_lse_merge(o_parts, l_parts, plan.n_split, false, out, lse, true, bhq, D, strm);
-    } else {
-      e = r3d::launch_attn_bf16(q, k, v, out, lse, stats, B, H, Sq, Skv, D, scale, chunk, out_bshd, 1, Skv, false,
-                                strm);
+    // A key split (the last round's tiles run as pieces over key ranges):
+    // their fp32 partials follow the statistics.
+    float* o_parts = nullptr;
+    float* l_parts = nullptr;
+    if (plan.ks.n_split > 1) {
+      o_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.stats_bytes);
+      l_parts = o_parts + plan.ks.n_split * plan.part_rows * D;
     }
+    e = r3d::launch_attn_bf16(q, k, v, out, lse, stats, B, H, Sq, Skv, D, scale, chunk, out_bshd, plan.ks, o_parts,
+                              l_parts, strm);
   } else
     e = r3d::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse, B, H, Sq, Skv,
                              D, scale, chunk, out_bshd, strm);

@@ -66,36 +66,50 @@ hipError_t launch_permute(const SegArgs& segs, void* out, bool bf16, int64_t B, 
 constexpr int kStatParts = 64;
 inline int64_t attn_stats_floats(int64_t B, int64_t H) { return 2 * B * H * kStatParts; }
 
+// Key split of a bf16 attention launch.  Query tiles are numbered head-major;
+// the first n_bulk run over all keys and write out / lse directly.  With
+// n_split > 1 each remaining tile runs n_split times, once per range of
+// split_len keys (a multiple of kv_chunk, or of the 128-key tile when
+// kv_chunk >= Skv), writing fp32 partials that an lse_merge combines into the
+// rows of those tiles.
+struct KeySplit {
+  int64_t n_bulk = 0;
+  int n_split = 1;
+  int64_t split_len = 0;
+};
+constexpr int kMaxKeySplit = 16;
+constexpr int64_t kMinSplitKeys = 512;
+
+// The split for a launch on a device with n_cus compute units: the tiles of
+// the last, partly filled round of blocks are split when a cost model of the
+// rounds (and of the partial writes and merge) says that is faster.
+KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                             int n_cus);
+// First row (of the [B*H*Sq] rows) of query tile n_bulk: the split tiles'
+// partials and merged rows start there.
+int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq);
+
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
-// instead of [B, H, Sq, D].  stats is a device workspace of
-// attn_stats_floats(B, H) floats, written by a pre-pass and read by the
-// attention kernel on `stream`.
-// n_split > 1: the keys are split into n_split ranges of split_len keys (a
-// multiple of kv_chunk, or of the 128-key tile when kv_chunk >= Skv), each
-// query tile runs once per range, and out / lse receive the fp32 partials
-// [n_split, B*H*Sq, D] / [n_split, B*H*Sq] (out_f32 true, out_bshd false),
-// for an lse_merge over the n_split parts.
+// instead of [B, H, Sq, D] (no key split then).  stats is a device workspace
+// of attn_stats_floats(B, H) floats, written by a pre-pass and read by the
+// attention kernel on `stream`.  With ks.n_split > 1, o_parts / l_parts hold
+// the pieces' partials [n_split, rows, D] / [n_split, rows] (rows = B*H*Sq -
+// attn_bf16_split_first_row(ks.n_bulk, Sq)) and the call ends with their merge.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                             float* stats, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
-                            float scale, int64_t kv_chunk, bool out_bshd, int n_split, int64_t split_len,
-                            bool out_f32, hipStream_t stream);
+                            float scale, int64_t kv_chunk, bool out_bshd, const KeySplit& ks, float* o_parts,
+                            float* l_parts, hipStream_t stream);
 
 // Query tiles per head and waves per block of the bf16 attention kernel (the
 // constant-max variant's flags take query_tiles * waves ints per head).
 int64_t attn_bf16_query_tiles(int64_t Sq);
 int attn_bf16_waves();
 
-// Number of key splits (1: none) for a bf16 attention launch on a device with
-// n_cus compute units, and *split_len: splitting only when the query tiles
-// alone leave the last round of blocks on the CUs mostly empty.
-constexpr int kMaxKeySplit = 8;
 // True when the launches of one bf16 attn_fwd call without a key split (the
 // statistics pre-pass and the attention grid) each stay within a 1-D grid's
-// 2^31 - 1 blocks and 2^32 work-items.  (A key split is only chosen for
-// grids of fewer than 4 blocks per CU.)
+// 2^31 - 1 blocks and 2^32 work-items.  (A split adds fewer than
+// kMaxKeySplit blocks per CU.)
 bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq);
-int attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_chunk, int n_cus,
-                        int64_t* split_len);
 
 // attn_fwd with a constant per-row softmax reference (the Cauchy-Schwarz
 // bound from the head's largest key norm).  stats as above; flags is a
