@@ -346,6 +346,12 @@ AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
   if (!out_bshd) p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
+  if (p.ks.n_split > 1) {  // the split grid must still fit a 1-D launch
+    const int64_t tiles = B * H * r3d::attn_bf16_query_tiles(Sq);
+    const int64_t blocks = p.ks.n_bulk + (tiles - p.ks.n_bulk) * p.ks.n_split;
+    if (blocks > (int64_t(1) << 31) - 1 || blocks * 64 * r3d::attn_bf16_waves() >= (int64_t(1) << 32))
+      p.unsplit(B, H, Sq, Skv);
+  }
   if (p.ks.n_split > 1) {
     p.part_rows = B * H * Sq - r3d::attn_bf16_split_first_row(p.ks.n_bulk, Sq);
     p.parts_bytes = ws_round(p.ks.n_split * p.part_rows * (D + 1) * 4);

@@ -362,36 +362,37 @@ def test_attn_key_split_small(gpu, D, B, H, Sq, Skv, kv_chunk):
     assert torch.equal(o2, out)
 
 
-@pytest.mark.parametrize("D,H,Sq,Skv,kv_chunk", [
-    (128, 36, 2800, 7900, 1000),   # 288 tiles: 256 whole, the last 32 as 8 ranges of one chunk (the last 900 keys)
-    (64, 40, 2700, 3000, 0),       # 320 tiles: 256 whole, 64 as 4 ranges of 6 tiles (the last 696 keys)
+@pytest.mark.parametrize("D,B,H,Sq,Skv,kv_chunk", [
+    (128, 1, 36, 2800, 7900, 1000),   # 288 tiles: 256 whole, the last 32 as 8 ranges of one chunk (the last 900 keys)
+    (64, 1, 40, 2700, 3000, 0),       # 320 tiles: 256 whole, 64 as 4 ranges of 6 tiles (the last 696 keys)
+    (128, 2, 18, 2800, 7900, 1000),   # as the first, the split starting in the second batch row
 ])
-def test_attn_tail_split_mixed_grid(gpu, D, H, Sq, Skv, kv_chunk):
+def test_attn_tail_split_mixed_grid(gpu, D, B, H, Sq, Skv, kv_chunk):
     """A grid with more query tiles than CUs and a thin last round: the first 256 tiles
     (a full round on the 256-CU chip) run over all keys and write out / lse directly; the
     tiles of the last round run as pieces over key ranges whose partials an lse_merge
     combines into those tiles' rows.  Every row of the last whole head and of each split
     head is checked against the oracle (tile boundaries, the first split tile, the ragged
     last tile of each head)."""
-    B = 1
     n_qt = -(-Sq // 384)
     stats_bytes = -(-(2 * B * H * 64 * 4) // 256) * 256
     ws = r3d.attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, torch.bfloat16)
     if torch.cuda.get_device_properties(gpu).multi_processor_count != 256:
         pytest.skip("the split of this grid is planned for a 256-CU device")
     assert ws > stats_bytes, "this grid is expected to split its last round"
-    first_split_head = 256 // n_qt
+    first_split_bh = 256 // n_qt                 # (batch, head) pairs counted head-major
     scale = 1.0 / math.sqrt(D)
     q = _rand((B, H, Sq, D), torch.bfloat16, 71)
     k = _rand((B, H, Skv, D), torch.bfloat16, 72)
     v = _rand((B, H, Skv, D), torch.bfloat16, 73)
     out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk)
     torch.cuda.synchronize()
-    heads = slice(first_split_head - 1, H)
-    say(f"tail split D={D} H={H}: heads {heads.start}..{H - 1} checked, split from head {first_split_head}")
-    ref_out, ref_lse = oracle.attention(to_f64(q[:, heads]), to_f64(k[:, heads]), to_f64(v[:, heads]), scale)
-    check_attn(out[:, heads].cpu(), lse[:, heads].cpu(), ref_out, ref_lse, torch.bfloat16,
-               f"tail split D={D} H={H} Sq={Sq} Skv={Skv} kv_chunk={kv_chunk}")
+    bh = slice(first_split_bh - 1, B * H)         # the last whole (batch, head) and every split one
+    say(f"tail split D={D} B={B} H={H}: (b,h) {bh.start}..{B * H - 1} checked, split from {first_split_bh}")
+    flat = lambda t: t.reshape(B * H, *t.shape[2:])[bh].unsqueeze(0)
+    ref_out, ref_lse = oracle.attention(to_f64(flat(q)), to_f64(flat(k)), to_f64(flat(v)), scale)
+    check_attn(flat(out).cpu(), flat(lse).cpu(), ref_out, ref_lse, torch.bfloat16,
+               f"tail split D={D} B={B} H={H} Sq={Sq} Skv={Skv} kv_chunk={kv_chunk}")
     # Without lse, the same result.
     o2 = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk, return_lse=False)
     assert torch.equal(o2, out)
