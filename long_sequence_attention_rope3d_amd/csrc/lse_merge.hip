@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__
   // The first kHeld parts' lse values are loaded together and kept in
   // registers (indices are compile-time, predicated on n, which is uniform);
   // parts beyond them (n > kHeld) are read again as needed.
-  constexpr int kHeld = 16, kG = 4;
+  // Data loads go out in groups of kG parts: all 16 held parts at once for
+  // fp32 parts (4.4% faster than groups of 4 on 13 parts, at 154 VGPRs), 4 for
+  // bf16 parts (16 at once was 33% slower there: the occupancy).
+  constexpr int kHeld = 16, kG = PBF16 ? 4 : 16;
   float lv[kHeld];
 #pragma unroll
   for (int j = 0; j < kHeld; ++j) lv[j] = j < n ? lse_parts[(int64_t)j * rows + row] : -INFINITY;
