@@ -398,6 +398,47 @@ def test_attn_tail_split_mixed_grid(gpu, D, B, H, Sq, Skv, kv_chunk):
     assert torch.equal(o2, out)
 
 
+def _random_attn_case(i):
+    """Seeded shape of random case i: a spread of B, H, Sq, Skv (ragged against the 384-row
+    and 128-key tiles), D, kv_chunk and scale; every fourth case has enough (batch, head)
+    pairs that its query tiles overflow one round of 256 blocks (a split last round)."""
+    g = np.random.default_rng(9000 + i)
+    D = int(g.choice([64, 128]))
+    B = int(g.integers(1, 4))
+    if i % 4 == 3:
+        Sq = int(g.integers(385, 1700))
+        H = int(-(-257 * 384 // (B * Sq)) + g.integers(0, 12))
+    else:
+        Sq = int(g.integers(1, 3000))
+        H = int(g.integers(1, 9))
+    Skv = int(g.integers(1, 9000))
+    kv_chunk = int(g.choice([0, int(g.integers(1, max(2, Skv)))]))
+    scale = float(g.choice([-1.0, 1.0]) * g.uniform(0.02, 0.25))
+    return B, H, Sq, Skv, D, kv_chunk, scale
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_attn_random_shapes(gpu, i):
+    """Seeded random shapes through the C ABI against the oracle on sampled rows (the first
+    and last row of every query tile of one head, then random rows anywhere)."""
+    B, H, Sq, Skv, D, kv_chunk, scale = _random_attn_case(i)
+    q = _rand((B, H, Sq, D), torch.bfloat16, 100 + 3 * i)
+    k = _rand((B, H, Skv, D), torch.bfloat16, 101 + 3 * i)
+    v = _rand((B, H, Skv, D), torch.bfloat16, 102 + 3 * i)
+    say(f"random case {i}: B={B} H={H} Sq={Sq} Skv={Skv} D={D} kv_chunk={kv_chunk} scale={scale:.4f} "
+        f"workspace {r3d.attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, torch.bfloat16)} B")
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(7000 + i)
+    bh = int(g.integers(0, B * H))
+    edges = np.unique(np.clip(np.concatenate([np.arange(0, Sq, 384), np.arange(383, Sq, 384), [Sq - 1]]), 0, Sq - 1))
+    rows = np.unique(np.concatenate([bh * Sq + edges, g.integers(0, B * H * Sq, 96)])).astype(np.int64)
+    ref_out, ref_lse = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), rows, scale)
+    idx = torch.from_numpy(rows).to(gpu)
+    check_attn(out.reshape(-1, D)[idx], lse.reshape(-1)[idx], ref_out, ref_lse, torch.bfloat16,
+               f"random case {i}")
+
+
 def test_attn_fwd_without_lse(gpu):
     q = _rand((1, 2, 150, 128), torch.bfloat16, 51).to(gpu)
     k = _rand((1, 2, 190, 128), torch.bfloat16, 52).to(gpu)
