@@ -165,6 +165,91 @@ def test_permute_with_fused_rope(gpu, dtype, D, grid):
     assert np.array_equal(_bits(out)[:, :, Nv:], want[:, :, Nv:])
 
 
+def _random_permute_case(i):
+    """Seeded re-layout case i: dtype, row width, B, H, a video grid (its token count is
+    segment 0's length), 0-3 joint segments of random length (zero included), RoPE split."""
+    g = np.random.default_rng(8000 + i)
+    dtype = [torch.bfloat16, torch.float32][int(g.integers(0, 2))]
+    D = int(g.choice([64, 128, 24])) if dtype == torch.bfloat16 else int(g.choice([64, 128]))
+    B, H = int(g.integers(1, 4)), int(g.integers(1, 30))
+    grid = tuple(int(x) for x in g.integers(1, 9, 3))
+    joint = [int(x) for x in g.integers(0, 300, int(g.integers(0, 4)))]
+    rope = D in (64, 128) and bool(g.integers(0, 2))
+    if rope:
+        dt = int(g.choice([0, D // 4]))
+        dh = 2 * int(g.integers(0, (D - dt) // 2 + 1))
+        split = (dt, dh, D - dt - dh)
+    else:
+        split = None
+    return dtype, D, B, H, grid, joint, split
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_permute_random(gpu, i):
+    """Seeded random re-layouts: the joint segments (and segment 0 without RoPE) bit-exact;
+    with RoPE, segment 0 within 1 ulp of the oracle's correctly rounded rotation and equal
+    to it but for at most 0.1% of the values (at least 2 allowed on small tensors)."""
+    dtype, D, B, H, grid, joint, split = _random_permute_case(i)
+    Nv = grid[0] * grid[1] * grid[2]
+    lens = [Nv] + joint
+    say(f"permute case {i}: {dtype} D={D} B={B} H={H} grid={grid} lens={lens} split={split}")
+    segs = [_rand((B, n, H, D), dtype, 200 + 5 * i + j) for j, n in enumerate(lens)]
+    out = r3d.joint_concat_permute([x.to(gpu) for x in segs], r3d.Rope3D(grid, split) if split else None).cpu()
+    want = oracle.joint_concat_permute([_bits(x) for x in segs])
+    if split is None:
+        assert np.array_equal(_bits(out), want)
+        return
+    assert np.array_equal(_bits(out)[:, :, Nv:], want[:, :, Nv:])
+    ref = oracle.rope3d(to_f64(segs[0]), grid, split, 10000.0)
+    ref = oracle.round_bf16(ref) if dtype == torch.bfloat16 else oracle.round_f32(ref)
+    got = to_f64(out[:, :, :Nv].transpose(1, 2).contiguous())
+    d = np.abs(got - ref)
+    if dtype == torch.bfloat16:
+        ulp = _bf16_ulp(ref)
+    else:
+        ax = np.abs(ref)
+        ulp = np.exp2(np.floor(np.log2(np.where(ax > 0, ax, 1.0))) - 23)
+    mism = int((d != 0).sum())
+    say(f"[permute case {i}] rope mismatches {mism} of {d.size}, max ulps {(d / ulp).max():.2f}")
+    assert (d <= ulp).all()
+    assert mism <= max(2, d.size // 1000)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_lse_merge_random(gpu, i):
+    """Seeded random merges: n parts (1-24), parts and output dtypes, row shapes, and parts
+    or whole rows without keys (lse = -inf)."""
+    g = np.random.default_rng(8500 + i)
+    n = int(g.integers(1, 25))
+    pd = [torch.float32, torch.bfloat16][int(g.integers(0, 2))]
+    od = [torch.float32, torch.bfloat16][int(g.integers(0, 2))]
+    B, H, S, D = int(g.integers(1, 3)), int(g.integers(1, 5)), int(g.integers(1, 700)), int(g.choice([64, 128]))
+    say(f"lse_merge case {i}: n={n} parts {pd} out {od} B={B} H={H} S={S} D={D}")
+    parts = _rand((n, B, H, S, D), pd, 300 + 2 * i)
+    lse = _rand((n, B, H, S), torch.float32, 301 + 2 * i, 4.0)
+    holes = torch.from_numpy(g.random((n, B, H, S)) < 0.2)
+    lse[holes] = -math.inf
+    lse[:, 0, 0, 0] = -math.inf          # one row with no keys at all
+    out, L = r3d.lse_merge(parts.to(gpu), lse.to(gpu), out_dtype=od)
+    ref_out, ref_L = oracle.lse_merge(to_f64(parts), to_f64(lse))
+    got = to_f64(out.cpu())
+    d = np.abs(got - ref_out)
+    if od == torch.float32:
+        assert d.max() <= 1e-5
+    else:
+        # The fp32 merge (absolute error within 1e-5, as the fp32 outputs show; it does not
+        # shrink with a result that cancels to near zero), then one RNE rounding to bfloat16.
+        r = d / (_bf16_ulp(ref_out) + 1e-5)
+        w = np.unravel_index(np.argmax(r), r.shape)
+        assert r.max() <= 1.0, f"{r.max():.2f} x tolerance at {w}: got {got[w]!r} want {ref_out[w]!r}"
+
+    gl = to_f64(L.cpu())
+    fin = np.isfinite(ref_L)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.abs(gl[fin] - ref_L[fin]).max() <= 1e-5
+    assert (got[0, 0, 0] == 0).all()
+
+
 # ------------------------------------------------------------------------------------------
 # QK-norm fused ahead of RoPE and the re-layout (r3d_joint_concat_permute_qknorm)
 # ------------------------------------------------------------------------------------------
