@@ -309,6 +309,41 @@ def test_permute_with_fused_qknorm(gpu, dtype, D, grid, split, B, H, lens, norme
         off += n
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_permute_qknorm_random(gpu, i):
+    """Seeded random QK-norm cases: H (beyond the chunks a thread holds too), D, weights of
+    random scale and sign, eps, input magnitudes from near eps to large, which segments are
+    normed, RoPE on or off; against prepare_qkv (norm stored, rotated, stored again)."""
+    g = np.random.default_rng(8800 + i)
+    dtype = torch.bfloat16 if i % 4 != 3 else torch.float32
+    D = int(g.choice([64, 128]))
+    B, H = int(g.integers(1, 3)), int(g.integers(1, 64))
+    grid = tuple(int(x) for x in g.integers(1, 6, 3))
+    Nv = grid[0] * grid[1] * grid[2]
+    lens = [Nv] + [int(x) for x in g.integers(0, 40, int(g.integers(0, 3)))]
+    normed = tuple(j for j in range(len(lens)) if g.random() < 0.7) or (0,)
+    rope = bool(g.integers(0, 2))
+    split = (D // 4, 3 * D // 8, 3 * D // 8)
+    mult = float(10.0 ** g.uniform(-3, 2))
+    eps = float(10.0 ** g.uniform(-8, -4))
+    say(f"qknorm case {i}: {dtype} D={D} B={B} H={H} lens={lens} normed={normed} rope={rope} "
+        f"mult={mult:.3g} eps={eps:.2g}")
+    segs = [_rand((B, n, H, D), dtype, 400 + 4 * i + j, mult) for j, n in enumerate(lens)]
+    gw = torch.Generator().manual_seed(900 + i)
+    wts = [(float(g.uniform(0.2, 3.0)) * torch.randn(H * D, generator=gw)) if j in normed else None
+           for j in range(len(lens))]
+    out = r3d.joint_concat_permute([x.to(gpu) for x in segs], r3d.Rope3D(grid, split) if rope else None,
+                                   norm=[w.to(gpu) if w is not None else None for w in wts], eps=eps)
+    torch.cuda.synchronize()
+    io = "bf16" if dtype == torch.bfloat16 else "f32"
+    ref, _, _ = oracle.prepare_qkv([to_f64(x) for x in segs], [to_f64(x) for x in segs],
+                                   [to_f64(x) for x in segs], grid if rope else (lens[0], 1, 1),
+                                   split if rope else (0, 0, D), 10000.0, io,
+                                   norm_q=[w.double().numpy() if w is not None else None for w in wts],
+                                   eps=eps)
+    check_prepared(out, ref, dtype, f"qknorm case {i}")
+
+
 # ------------------------------------------------------------------------------------------
 # attn_fwd on small shapes: full tensors
 # ------------------------------------------------------------------------------------------
