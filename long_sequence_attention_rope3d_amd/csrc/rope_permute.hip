@@ -83,6 +83,10 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
   return ((f & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : (f >> 16);
 }
 
+// Zero or subnormal binary32: one v_cmp_class_f32 (classes -denorm, -0, +0,
+// +denorm), the same set whether or not the mode flushes subnormals.
+__device__ __forceinline__ bool zero_or_subnormal(float f) { return __builtin_amdgcn_classf(f, 0xf0); }
+
 // Two binary64 values -> two bfloat16 (y0 in the low half), each rounded
 // to nearest-even exactly as f64_to_bf16 does, mostly in hardware: RNE to
 // binary32 (v_cvt_f32_f64), then the packed binary32 -> bfloat16 RNE
@@ -95,8 +99,8 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double y) {
 __device__ __forceinline__ uint32_t f64x2_to_bf16x2(double y0, double y1) {
   const float f0 = (float)y0, f1 = (float)y1;
   const uint32_t u0 = __float_as_uint(f0), u1 = __float_as_uint(f1);
-  const bool slow = ((u0 & 0xffffu) == 0x8000u) | ((u1 & 0xffffu) == 0x8000u) | ((u0 & 0x7f800000u) == 0u) |
-                    ((u1 & 0x7f800000u) == 0u);
+  const bool slow = ((u0 & 0xffffu) == 0x8000u) | ((u1 & 0xffffu) == 0x8000u) | zero_or_subnormal(f0) |
+                    zero_or_subnormal(f1);
   if (__builtin_expect(slow, 0)) return f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{f0, f1}, bf16x2_t));
 }
@@ -148,7 +152,7 @@ __device__ __forceinline__ u32x4 norm_chunk(u32x4 v, double r, float4 wa, float4
       const float y0 = x0 * r32 * w[2 * q], y1 = x1 * r32 * w[2 * q + 1];
       const uint32_t u0 = __float_as_uint(y0), u1 = __float_as_uint(y1);
       const bool slow = (((u0 - 0x7ffcu) & 0xffffu) <= 8u) | (((u1 - 0x7ffcu) & 0xffffu) <= 8u) |
-                        ((u0 & 0x7f800000u) == 0u) | ((u1 & 0x7f800000u) == 0u);
+                        zero_or_subnormal(y0) | zero_or_subnormal(y1);
       if (__builtin_expect(slow, 0))
         v[q] = f64_to_bf16((double)x0 * r * (double)w[2 * q]) |
                (f64_to_bf16((double)x1 * r * (double)w[2 * q + 1]) << 16);
