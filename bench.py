@@ -14,7 +14,8 @@ attn_fwd).  `value` is attention TFLOP/s over the whole step, counting
 4*B*H*Sq*Skv*D flops per step.  The standalone rope3d_apply and lse_merge
 entry points are timed after the step loop on the same workload shapes and
 reported under "kernels", with the shard-shape proxies, attn_fwd on the
-lite-clip and image-dit workloads (their own seeded inputs and kv_chunk) and
+tiny (fp32), lite-clip and image-dit workloads (their own seeded inputs and
+kv_chunk) and
 on the long-video workload (GPU-drawn inputs with its outlier keys).
 
 roofline.achieved is 4*B*H*Sq*Skv*D over the mean duration of the timed
@@ -41,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MI355X_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+MI355X_FP32_PEAK_TFLOPS = 157.3    # fp32 (the tiny workload's path runs in fp32)
 MI355X_HBM_GBPS = 8000.0
 METRIC = "attention TFLOP/s (4·B·H·Sq·Skv·D) + % bf16 MFMA peak; ms/call at 52k tokens"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_traffic.md")
@@ -196,7 +198,7 @@ def main():
     if not args.no_kernels:
         kernels = time_side_kernels(torch, r3d, w, segs, q, k, v, lse, rope, dev, stream)
         if w.name == "pro-clip":
-            for other in ("lite-clip", "image-dit"):
+            for other in ("tiny", "lite-clip", "image-dit"):
                 kernels["attn_fwd_" + other.replace("-", "_")] = time_attn_workload(torch, r3d, other, dev, stream)
             if not args.no_long_video:
                 kernels["attn_fwd_long_video"] = time_long_video(torch, r3d, dev, stream)
@@ -369,8 +371,14 @@ def time_attn_workload(torch, r3d, name, dev, stream, reps: int = 20):
     med = ms[len(ms) // 2]
     tf = w.attn_flops / (med * 1e-3) / 1e12
     log(f"attn_fwd_{w.name}: {med:.4f} ms (min {ms[0]:.4f}), {tf:.1f} TFLOP/s")
-    return {"ms": round(med, 4), "ms_min": round(ms[0], 4), "S": w.S, "H": w.H, "kv_chunk": w.kv_chunk,
-            "TFLOPs": round(tf, 2), "frac_bf16_peak": round(tf / MI355X_BF16_PEAK_TFLOPS, 4)}
+    res = {"ms": round(med, 4), "ms_min": round(ms[0], 4), "S": w.S, "H": w.H, "kv_chunk": w.kv_chunk,
+           "TFLOPs": round(tf, 3)}
+    if w.dtype == "bf16":
+        res["frac_bf16_peak"] = round(tf / MI355X_BF16_PEAK_TFLOPS, 4)
+    else:
+        res["dtype"] = w.dtype
+        res["frac_fp32_peak"] = round(tf / MI355X_FP32_PEAK_TFLOPS, 5)
+    return res
 
 
 def time_long_video(torch, r3d, dev, stream, reps: int = 3):
