@@ -32,9 +32,12 @@
 // * Block = 12 waves = 384 query rows (32 per wave), one block per CU, i.e.
 //   three waves per SIMD: while one wave of a SIMD runs its softmax on the
 //   VALU or waits on LDS, the others keep the matrix core busy.  That caps a
-//   wave at 168 registers (the kernel needs 162 and spills nothing).  384
+//   wave at 168 registers (the kernel needs 160 and spills nothing).  384
 //   also divides the 52608-token workload exactly, and 137 query tiles per
-//   head keep the last round of blocks on the CUs nearly full.
+//   head keep the last round of blocks on the CUs nearly full.  A grid of
+//   few query tiles (fewer than the CUs) may instead take blocks of 8 waves =
+//   256 rows, two waves per SIMD (up to 256 registers): 10% slower per CU,
+//   but more of the CUs busy (the same kernel, instantiated for 8 waves).
 // * Grid = one block per query tile (B*H*ceil(Sq/384) tiles), plus n_split
 //   blocks per tile of a split last round in place of one; re-numbered so
 //   consecutive query tiles over the same keys land on the same XCD
@@ -101,13 +104,20 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef R3D_ATTN_STAGES
 #define R3D_ATTN_STAGES 2
 #endif
-constexpr int kWaves = R3D_ATTN_WAVES;
+constexpr int kWaves = R3D_ATTN_WAVES;  // the block of every launch but small grids'
+constexpr int kWavesSmall = 8;          // the block a grid of few query tiles may take instead
 constexpr int kStages = R3D_ATTN_STAGES;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per block
-constexpr int kWavesPerSimd = kWaves / 4;  // waves per SIMD (one block per CU)
-static_assert(kWaves % 4 == 0, "whole waves per SIMD");
-static_assert(kAttnMaxSeq + kBM <= INT32_MAX, "query rows fit in 32 bits");
+// Block of W waves: 64 W threads, 32 W query rows, W / 4 waves per SIMD (one
+// block per CU).
+template <int W>
+struct Blk {
+  static_assert(W % 4 == 0, "whole waves per SIMD");
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBM = 32 * W;  // query rows per block
+  static constexpr int kWavesPerSimd = W / 4;
+};
+static_assert(kAttnMaxSeq + Blk<kWaves>::kBM <= INT32_MAX, "query rows fit in 32 bits");
+static_assert(kAttnMaxSeq + Blk<kWavesSmall>::kBM <= INT32_MAX, "query rows fit in 32 bits");
 static_assert(kStages == 2 || kStages == 3, "2 or 3 stages");
 #ifndef R3D_ATTN_BN
 #define R3D_ATTN_BN 128
@@ -118,18 +128,18 @@ constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
 constexpr int kSlackMax = 32;     // largest bound slack under which the row max is skipped, log2 units
 
-template <int D>
+template <int D, int W>
 struct Geom {
   static constexpr int kSteps = D / 16;               // MFMA k-steps of Q K^T
   static constexpr int kDBlk = D / 32;                // 32-wide d blocks of O^T
   static constexpr int kCpr = D / 8;                  // 16-byte chunks per K/V row
   static constexpr int kTile = kBN * D;               // elements of one K or V tile
   static constexpr int kDma = kBN * kCpr / 64;         // 1 KB DMA instructions per tensor per tile
-  static constexpr int kDmaPerWave = (kDma + kWaves - 1) / kWaves;  // the last may be partial
-  static_assert(kDma >= kWaves, "every wave copies");
+  static constexpr int kDmaPerWave = (kDma + W - 1) / W;  // the last may be partial
+  static_assert(kDma >= W, "every wave copies");
   // With a tile left in flight across the barrier (3 stages) every wave must
   // issue the same number of copies for its vmcnt wait to cover the older tile.
-  static_assert(kStages == 2 || kDma % kWaves == 0, "uneven copy split needs 2 stages");
+  static_assert(kStages == 2 || kDma % W == 0, "uneven copy split needs 2 stages");
 };
 
 // Per-row XOR swizzles of the 16-byte chunk index (see the bank notes above).
@@ -227,21 +237,21 @@ struct TileCursor {
 // + barrier that retire that stage's copies).  The compiler's own vmcnt waits
 // (the Q loads) only become stricter by the extra operations in the counter.
 // One wait state separates the M0 write from the DMA.
-template <int D, bool IS_V, bool kFull>
+template <int D, int W, bool IS_V, bool kFull>
 __device__ __forceinline__ void dma_tile(uint32_t lds_tile, const uint16_t* src, int n, int wave, int lane) {
-  using G = Geom<D>;
-  // Instruction i of a wave covers slots 64*(wave + kWaves*i) + [0, 64): rows
+  using G = Geom<D, W>;
+  // Instruction i of a wave covers slots 64*(wave + W*i) + [0, 64): rows
   // r0 + kRowStep*i.  The swizzles depend on row bits that kRowStep leaves
   // unchanged, so the chunk (and for full tiles the whole per-lane offset) is
   // the same for every i; instruction i adds kRowStep rows (8 KB) to the
   // wave-uniform global base and to M0.
-  constexpr int kRowStep = 64 * kWaves / G::kCpr;
+  constexpr int kRowStep = 64 * W / G::kCpr;
   static_assert(swz_periodic<D, IS_V>(kRowStep), "swizzle must be invariant under a step of kRowStep rows");
   const int r0 = (64 * wave + lane) / G::kCpr;
   const int cl = (lane % G::kCpr) ^ (IS_V ? swz_v<D>(r0) : swz_k<D>(r0));
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    if (G::kDma % kWaves != 0 && wave + kWaves * i >= G::kDma) break;  // wave-uniform
+    if (G::kDma % W != 0 && wave + W * i >= G::kDma) break;  // wave-uniform
     // Full tile: base advanced by i*kRowStep rows, offset of row r0.  Short
     // tile: base at the tile, offset of the clamped absolute row.  Either way
     // the unsigned 32-bit offset is the in-bounds row's distance from base.
@@ -257,7 +267,7 @@ __device__ __forceinline__ void dma_tile(uint32_t lds_tile, const uint16_t* src,
     const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
     const uint64_t base = (uint64_t)b_lo | ((uint64_t)b_hi << 32);
     const uint32_t lds =
-        (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_tile + (uint32_t)((wave + kWaves * i) * 64 * 16)));
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_tile + (uint32_t)((wave + W * i) * 64 * 16)));
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                  : "memory", "m0");
   }
@@ -305,14 +315,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // (about 87 in natural-log units); each wave flags, per block tile, rows whose
 // row sum fell below 2^-100 or whose output is not finite, and a second
 // launch of the online kernel (fix_flags) recomputes exactly those tiles.
-template <int D, bool kConstMax>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
+template <int D, bool kConstMax, int W>
+__global__ __launch_bounds__(Blk<W>::kThreads, Blk<W>::kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ out, float* __restrict__ lse, int64_t H, int64_t Sq, int64_t Skv, float c,
     uint32_t qsign, int64_t chunk, int n_qt, int n_tiles, int n_bulk, int out_bshd, const float* __restrict__ stats,
     int n_split, int64_t split_len, float* __restrict__ o_parts, float* __restrict__ l_parts, int64_t tail_row0,
     int chunk_bits, int* __restrict__ flags_out, const int* __restrict__ fix_flags) {
-  using G = Geom<D>;
+  using G = Geom<D, W>;
+  constexpr int kBM = Blk<W>::kBM;
   // K/V stage buffers (the third only with kStages == 3).
   // K/V stage buffers in one array, K stages first: [K_0 .. K_{kStages-1} | V_0 .. V_{kStages-1}].
   // A DS instruction's immediate offset has 16 bits, so every operand read
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
   // flagged.  Every wave reads the same flags, so the whole block leaves
   // together, before its first barrier.
   if (!kConstMax && fix_flags) {
-    const int f = lane < kWaves ? fix_flags[(int64_t)logical * kWaves + lane] : 0;
+    const int f = lane < W ? fix_flags[(int64_t)logical * W + lane] : 0;
     if (__ballot(f != 0) == 0) return;
   }
   const int qrow = qt * kBM + wave * 32 + r32;  // < Sq + kBM <= 2^31
@@ -471,11 +482,11 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     const uint16_t* ks = kb + (int64_t)pf.kv0 * D;
     const uint16_t* vs = vb + (int64_t)pf.kv0 * D;
     if (n == kBN) {
-      dma_tile<D, false, true>(lk, ks, n, wave, lane);
-      dma_tile<D, true, true>(lv, vs, n, wave, lane);
+      dma_tile<D, W, false, true>(lk, ks, n, wave, lane);
+      dma_tile<D, W, true, true>(lv, vs, n, wave, lane);
     } else {
-      dma_tile<D, false, false>(lk, ks, n, wave, lane);
-      dma_tile<D, true, false>(lv, vs, n, wave, lane);
+      dma_tile<D, W, false, false>(lk, ks, n, wave, lane);
+      dma_tile<D, W, true, false>(lv, vs, n, wave, lane);
     }
     pf.advance(chunk32, kv_end);
   };
@@ -649,7 +660,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_bf16_kernel(
     m_run += log2f(l_tot);
     const bool any_bad = __ballot(bad) != 0;
     if (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0)
-      flags_out[(int64_t)logical * kWaves + wave] = any_bad ? 1 : 0;
+      flags_out[(int64_t)logical * W + wave] = any_bad ? 1 : 0;
   }
 
   // ---- epilogue: out (bf16, RNE; or an fp32 partial for a piece) and lse (natural log) ----
@@ -767,17 +778,18 @@ hipError_t launch_head_stats(const uint16_t* kp, const uint16_t* vp, float* stat
   return hipGetLastError();
 }
 
-template <bool kConstMax>
-hipError_t launch_attn_kernel(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                              int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
-                              bool out_bshd, const float* stats, const KeySplit& ks, float* o_parts,
-                              float* l_parts, int* flags_out, const int* fix_flags, hipStream_t stream) {
+template <bool kConstMax, int W>
+hipError_t launch_attn_kernel_w(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
+                                bool out_bshd, const float* stats, const KeySplit& ks, float* o_parts,
+                                float* l_parts, int* flags_out, const int* fix_flags, hipStream_t stream) {
+  constexpr int kBM = Blk<W>::kBM;
   const int n_qt = (int)((Sq + kBM - 1) / kBM);
   const int n_tiles = (int)(B * H * n_qt);
   const int n_split = ks.n_split > 1 ? ks.n_split : 1;
   const int n_bulk = n_split > 1 ? (int)ks.n_bulk : n_tiles;
   const int n_blocks = n_bulk + (n_tiles - n_bulk) * n_split;
-  const int64_t tail_row0 = attn_bf16_split_first_row(n_bulk, Sq);
+  const int64_t tail_row0 = attn_bf16_split_first_row(n_bulk, Sq, W);
   const float c = fabsf(scale) * 1.44269504088896340736f;  // |scale| * log2(e)
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
   // Longest run of keys accumulated without a merge: a chunk (within a key
@@ -789,14 +801,27 @@ hipError_t launch_attn_kernel(const void* q, const void* k, const void* v, void*
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
   if (D == 64)
-    attn_bf16_kernel<64, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
+    attn_bf16_kernel<64, kConstMax, W><<<n_blocks, Blk<W>::kThreads, 0, stream>>>(
         qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_tiles, n_bulk, out_bshd ? 1 : 0, stats,
         n_split, ks.split_len, o_parts, l_parts, tail_row0, chunk_bits, flags_out, fix_flags);
   else
-    attn_bf16_kernel<128, kConstMax><<<n_blocks, kThreads, 0, stream>>>(
+    attn_bf16_kernel<128, kConstMax, W><<<n_blocks, Blk<W>::kThreads, 0, stream>>>(
         qp, kp, vp, out, lse, H, Sq, Skv, c, qsign, kv_chunk, n_qt, n_tiles, n_bulk, out_bshd ? 1 : 0, stats,
         n_split, ks.split_len, o_parts, l_parts, tail_row0, chunk_bits, flags_out, fix_flags);
   return hipGetLastError();
+}
+
+template <bool kConstMax>
+hipError_t launch_attn_kernel(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                              int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
+                              bool out_bshd, const float* stats, const KeySplit& ks, float* o_parts,
+                              float* l_parts, int* flags_out, const int* fix_flags, hipStream_t stream) {
+  if (!kConstMax && ks.waves == kWavesSmall)
+    return launch_attn_kernel_w<kConstMax, kWavesSmall>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk,
+                                                        out_bshd, stats, ks, o_parts, l_parts, flags_out,
+                                                        fix_flags, stream);
+  return launch_attn_kernel_w<kConstMax, kWaves>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd,
+                                                 stats, ks, o_parts, l_parts, flags_out, fix_flags, stream);
 }
 
 }  // namespace
@@ -806,64 +831,90 @@ bool attn_bf16_launches_fit(int64_t B, int64_t H, int64_t Sq) {
     return blocks > 0 && blocks <= (int64_t(1) << 31) - 1 && blocks * threads < (int64_t(1) << 32);
   };
   const int64_t nbh = B * H;
-  return fits(nbh * kStatParts, kNormThreads) && fits(nbh * ((Sq + kBM - 1) / kBM), kThreads);
+  return fits(nbh * kStatParts, kNormThreads) &&
+         fits(nbh * ((Sq + Blk<kWaves>::kBM - 1) / Blk<kWaves>::kBM), Blk<kWaves>::kThreads);
 }
 
-int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq) {
-  const int64_t n_qt = (Sq + kBM - 1) / kBM;
-  return (n_bulk / n_qt) * Sq + (n_bulk % n_qt) * kBM;
+int64_t attn_bf16_query_tiles(int64_t Sq, int waves) {
+  const int64_t bm = 32 * (int64_t)waves;
+  return (Sq + bm - 1) / bm;
 }
 
-KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
-                             int n_cus) {
-  const int64_t n_qt = (Sq + kBM - 1) / kBM;
-  const int64_t tiles = B * H * n_qt;
-  KeySplit none;
-  none.n_bulk = tiles;
-  none.n_split = 1;
-  none.split_len = Skv;
-  if (n_cus <= 0) return none;
-  const int64_t tail = tiles % n_cus;  // tiles of the last, partly filled round
-  if (tail == 0) return none;
-  const int64_t full = tiles / n_cus;
-  // Cost model, in units of one tile over all Skv keys on a fully busy chip,
-  // fitted to timings of forced splits on the MI355X (shard shapes, image and
-  // long-video workloads).  A round that fills a share f of the CUs costs
-  // 0.83 + 0.17 f of a full one: the chip is power-limited and clocks up when
-  // fewer CUs run, but not by much.  A piece of len keys costs like len + 700
-  // keys (prologue, pipeline fill, partial write); the partials' write and
-  // merge stream at ~5 TB/s.
+int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq, int waves) {
+  const int64_t bm = 32 * (int64_t)waves;
+  const int64_t n_qt = (Sq + bm - 1) / bm;
+  return (n_bulk / n_qt) * Sq + (n_bulk % n_qt) * bm;
+}
+
+namespace {
+// The best key split for blocks of `waves` waves, and its modelled time in
+// seconds.  Cost model fitted to timings of forced splits on the MI355X
+// (shard shapes, image and long-video workloads): a round of blocks that
+// fills a share f of the CUs costs 0.83 + 0.17 f of a full one (the chip is
+// power-limited and clocks up when fewer CUs run, but not by much); a piece
+// of len keys costs like len + 700 keys (prologue, pipeline fill, partial
+// write); the partials' write and merge stream at ~5 TB/s; a split must gain
+// 2%.  A block of 12 waves works at ~1250 TFLOP/s over the chip; one of 8
+// waves at 0.9 of that rate per CU (two waves per SIMD hide less).
+KeySplit plan_waves(int waves, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                    int n_cus, double* seconds) {
+  const int64_t bm = 32 * (int64_t)waves;
+  const int64_t tiles = B * H * attn_bf16_query_tiles(Sq, waves);
+  const double eff = waves == kWaves ? 1.0 : 0.9;
+  const double tile_s = 4.0 * bm * (double)Skv * (double)D / (1250e12 / n_cus) / eff;  // one tile, all keys
   auto round_cost = [](double f) { return 0.83 + 0.17 * f; };
   auto rounds = [&](int64_t nb, double len) {  // nb blocks of relative length len
     const int64_t r = nb / n_cus, f = nb % n_cus;
     return len * ((double)r + (f ? round_cost((double)f / n_cus) : 0.0));
   };
-  const double base = (double)full + round_cost((double)tail / n_cus);
-  // Seconds of one tile at the kernel's rate (~1250 TFLOP/s over the chip).
-  const double tile_s = 4.0 * kBM * (double)Skv * (double)D / (1250e12 / n_cus);
-  const double tail_rows = (double)(B * H * Sq - attn_bf16_split_first_row(tiles - tail, Sq));
+  KeySplit best;
+  best.waves = waves;
+  best.n_bulk = tiles;
+  best.n_split = 1;
+  best.split_len = Skv;
+  const int64_t tail = tiles % n_cus;  // tiles of the last, partly filled round
+  const int64_t full = tiles / n_cus;
+  const double base = ((double)full + (tail ? round_cost((double)tail / n_cus) : 0.0)) * tile_s;
+  *seconds = base;
+  if (tail == 0) return best;
+  const double tail_rows = (double)(B * H * Sq - attn_bf16_split_first_row(tiles - tail, Sq, waves));
   const int64_t unit = kv_chunk < Skv ? kv_chunk : kBN;  // ranges hold whole chunks, else whole tiles
   const int64_t n_units = (Skv + unit - 1) / unit;
-  KeySplit best = none;
-  double best_cost = base;
   for (int s = 2; s <= kMaxKeySplit; ++s) {
     const int64_t len = ((n_units + s - 1) / s) * unit;
     if (len < kMinSplitKeys) break;
     const int64_t n = (Skv + len - 1) / len;  // ranges actually made
     if (n < 2) continue;
     const double merge_s = ((double)n * tail_rows * (D + 1) * 4.0 * 2.0 + tail_rows * D * 2.0) / 5e12 + 10e-6;
-    const double cost = (double)full + rounds(tail * n, (double)(len + 700) / (double)Skv) + merge_s / tile_s;
-    if (cost < base * 0.98 && cost < best_cost) {  // a split must gain 2%
+    const double cost =
+        ((double)full + rounds(tail * n, (double)(len + 700) / (double)Skv)) * tile_s + merge_s;
+    if (cost < base * 0.98 && cost < *seconds) {
       best.n_bulk = tiles - tail;
       best.n_split = (int)n;
       best.split_len = len;
-      best_cost = cost;
+      *seconds = cost;
     }
   }
   return best;
 }
+}  // namespace
 
-int64_t attn_bf16_query_tiles(int64_t Sq) { return (Sq + kBM - 1) / kBM; }
+KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                             int n_cus) {
+  KeySplit none;
+  none.waves = kWaves;
+  none.n_bulk = B * H * attn_bf16_query_tiles(Sq, kWaves);
+  none.n_split = 1;
+  none.split_len = Skv;
+  if (n_cus <= 0) return none;
+  double t_big = 0.0, t_small = 0.0;
+  const KeySplit big = plan_waves(kWaves, B, H, Sq, Skv, D, kv_chunk, n_cus, &t_big);
+  if (D != 128) return big;  // the 8-wave block's rate was measured at D = 128
+  const KeySplit small = plan_waves(kWavesSmall, B, H, Sq, Skv, D, kv_chunk, n_cus, &t_small);
+  // The smaller block only for grids it clearly serves better (few query
+  // tiles: the larger block leaves CUs idle).
+  return t_small < 0.98 * t_big ? small : big;
+}
 
 int attn_bf16_waves() { return kWaves; }
 
@@ -878,7 +929,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                                 l_parts, nullptr, nullptr, stream);
   if (e != hipSuccess || ks.n_split <= 1) return e;
   // Merge the pieces' partials into the rows of the split tiles.
-  const int64_t row0 = attn_bf16_split_first_row(ks.n_bulk, Sq);
+  const int64_t row0 = attn_bf16_split_first_row(ks.n_bulk, Sq, ks.waves);
   return launch_lse_merge(o_parts, l_parts, ks.n_split, false, static_cast<uint16_t*>(out) + row0 * D,
                           lse ? lse + row0 : nullptr, true, B * H * Sq - row0, D, stream);
 }
@@ -890,7 +941,8 @@ hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v
                                    Skv, D, stream);
   if (e != hipSuccess) return e;
   KeySplit whole;
-  whole.n_bulk = B * H * ((Sq + kBM - 1) / kBM);
+  whole.waves = kWaves;
+  whole.n_bulk = B * H * attn_bf16_query_tiles(Sq, kWaves);
   whole.n_split = 1;
   whole.split_len = Skv;
   e = launch_attn_kernel<true>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, Skv, false, stats, whole, nullptr,

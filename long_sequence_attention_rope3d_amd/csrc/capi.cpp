@@ -331,7 +331,8 @@ struct AttnPlan {
   int64_t stats_bytes = 0, parts_bytes = 0, part_rows = 0;
   int64_t total() const { return stats_bytes + parts_bytes; }
   void unsplit(int64_t B, int64_t H, int64_t Sq, int64_t Skv) {
-    ks.n_bulk = B * H * r3d::attn_bf16_query_tiles(Sq);
+    ks.waves = r3d::attn_bf16_waves();
+    ks.n_bulk = B * H * r3d::attn_bf16_query_tiles(Sq, ks.waves);
     ks.n_split = 1;
     ks.split_len = Skv;
     parts_bytes = part_rows = 0;
@@ -346,21 +347,20 @@ AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
   if (!out_bshd) p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
-  if (p.ks.n_split > 1) {  // the split grid must still fit a 1-D launch
-    const int64_t tiles = B * H * r3d::attn_bf16_query_tiles(Sq);
-    const int64_t blocks = p.ks.n_bulk + (tiles - p.ks.n_bulk) * p.ks.n_split;
-    if (blocks > (int64_t(1) << 31) - 1 || blocks * 64 * r3d::attn_bf16_waves() >= (int64_t(1) << 32))
-      p.unsplit(B, H, Sq, Skv);
+  {  // the planned grid must still fit a 1-D launch
+    const int64_t tiles = B * H * r3d::attn_bf16_query_tiles(Sq, p.ks.waves);
+    const int64_t blocks = p.ks.n_split > 1 ? p.ks.n_bulk + (tiles - p.ks.n_bulk) * p.ks.n_split : tiles;
+    if (blocks > (int64_t(1) << 31) - 1 || blocks * 64 * p.ks.waves >= (int64_t(1) << 32)) p.unsplit(B, H, Sq, Skv);
   }
   if (p.ks.n_split > 1) {
-    p.part_rows = B * H * Sq - r3d::attn_bf16_split_first_row(p.ks.n_bulk, Sq);
+    p.part_rows = B * H * Sq - r3d::attn_bf16_split_first_row(p.ks.n_bulk, Sq, p.ks.waves);
     p.parts_bytes = ws_round(p.ks.n_split * p.part_rows * (D + 1) * 4);
   }
   return p;
 }
 
 int64_t constmax_flags_ints(int64_t B, int64_t H, int64_t Sq) {
-  return B * H * r3d::attn_bf16_query_tiles(Sq) * r3d::attn_bf16_waves();
+  return B * H * r3d::attn_bf16_query_tiles(Sq, r3d::attn_bf16_waves()) * r3d::attn_bf16_waves();
 }
 
 // Shared by both output layouts: the validation is identical (out has the

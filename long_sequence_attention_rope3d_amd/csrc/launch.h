@@ -73,6 +73,7 @@ inline int64_t attn_stats_floats(int64_t B, int64_t H) { return 2 * B * H * kSta
 // kv_chunk >= Skv), writing fp32 partials that an lse_merge combines into the
 // rows of those tiles.
 struct KeySplit {
+  int waves = 12;  // waves per block: 32 * waves query rows per tile (12, or 8 for grids of few tiles)
   int64_t n_bulk = 0;
   int n_split = 1;
   int64_t split_len = 0;
@@ -80,29 +81,31 @@ struct KeySplit {
 constexpr int kMaxKeySplit = 16;
 constexpr int64_t kMinSplitKeys = 512;
 
-// The split for a launch on a device with n_cus compute units: the tiles of
-// the last, partly filled round of blocks are split when a cost model of the
-// rounds (and of the partial writes and merge) says that is faster.
+// The block shape and split for a launch on a device with n_cus compute
+// units: the tiles of the last, partly filled round of blocks are split when
+// a cost model of the rounds (and of the partial writes and merge) says that
+// is faster, and a grid of few query tiles may take 8-wave blocks.
 KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
                              int n_cus);
-// First row (of the [B*H*Sq] rows) of query tile n_bulk: the split tiles'
-// partials and merged rows start there.
-int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq);
+// First row (of the [B*H*Sq] rows) of query tile n_bulk for blocks of
+// `waves` waves: the split tiles' partials and merged rows start there.
+int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq, int waves);
 
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
 // instead of [B, H, Sq, D] (no key split then).  stats is a device workspace
 // of attn_stats_floats(B, H) floats, written by a pre-pass and read by the
 // attention kernel on `stream`.  With ks.n_split > 1, o_parts / l_parts hold
 // the pieces' partials [n_split, rows, D] / [n_split, rows] (rows = B*H*Sq -
-// attn_bf16_split_first_row(ks.n_bulk, Sq)) and the call ends with their merge.
+// attn_bf16_split_first_row(ks.n_bulk, Sq, ks.waves)) and the call ends with their merge.
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* out, float* lse,
                             float* stats, int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                             float scale, int64_t kv_chunk, bool out_bshd, const KeySplit& ks, float* o_parts,
                             float* l_parts, hipStream_t stream);
 
-// Query tiles per head and waves per block of the bf16 attention kernel (the
-// constant-max variant's flags take query_tiles * waves ints per head).
-int64_t attn_bf16_query_tiles(int64_t Sq);
+// Query tiles per head for blocks of `waves` waves, and the waves per block
+// of every launch but small grids' (the constant-max variant always uses it;
+// its flags take query_tiles * waves ints per head).
+int64_t attn_bf16_query_tiles(int64_t Sq, int waves);
 int attn_bf16_waves();
 
 // True when the launches of one bf16 attn_fwd call without a key split (the
