@@ -2,86 +2,110 @@
 //
 // Same blockwise algorithm as the bf16 MFMA path, in plain fp32 VALU code:
 // keys are visited chunk by chunk; inside a chunk an online softmax keeps a
-// running max m, sum l and accumulator acc (rescaled per key tile); at the end
-// of every chunk (O_c = acc/l, lse_c = m + ln l) is merged into the running
-// result by the log-sum-exp rule
+// running max m, sum l and accumulator acc (rescaled per 64-key block); at
+// the end of every chunk (O_c = acc/l, lse_c = m + ln l) is merged into the
+// running result by the log-sum-exp rule
 //   L' = ln(e^L + e^lse_c),  O = O e^(L - L') + O_c e^(lse_c - L').
 // ("Context Parallelism in vLLM Omni Neuron", §Self-Attention, §Ring
 // attention, §Memory and Compute Benefits.)
 //
-// One thread per query row, 64 rows per block; key/value tiles of kBN rows are
-// staged in LDS and read by every thread with broadcast (same-address) loads.
-// The merged result O lives in LDS (one padded row per thread), the chunk
-// accumulator in registers.
+// One wave per query row, four rows of one head per block; the block stages
+// 64-key tiles of K and V in LDS.  For a tile, lane j forms key j's logit
+// against the row's query (read from LDS as a broadcast), the wave reduces
+// the tile's max and sum, writes the tile's p to LDS, and lane l accumulates
+// d = l (and l + 64 for D = 128) of P V.  K rows are padded to D + 4 floats
+// so that the 16-byte reads of 16 lanes (16 different rows, same columns)
+// fall into distinct banks; V rows are read along d, conflict-free.
 #include "launch.h"
 
 namespace r3d {
 namespace {
 
-constexpr int kRows = 64;
-constexpr int kBN = 16;
+constexpr int kRowsF32 = 4;          // query rows (waves) per block
+constexpr int kBNF32 = 64;           // keys per tile: one per lane
+constexpr int kThreadsF32 = 64 * kRowsF32;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
 
 template <int D>
-__global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                         const float* __restrict__ v, float* __restrict__ out,
-                                                         float* __restrict__ lse, int64_t H, int64_t Sq,
-                                                         int64_t Skv, float scale, int64_t chunk, int64_t n_qt,
-                                                         int out_bshd) {
-  __shared__ float ks[kBN][D];
-  __shared__ float vs[kBN][D];
-  __shared__ float orun[kRows][D + 1];
-  const int t = threadIdx.x;
+__global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                               const float* __restrict__ v, float* __restrict__ out,
+                                                               float* __restrict__ lse, int64_t H, int64_t Sq,
+                                                               int64_t Skv, float scale, int64_t chunk, int64_t n_qt,
+                                                               int out_bshd) {
+  constexpr int E = D / 64;    // d values per lane
+  constexpr int KP = D + 4;    // padded K row (floats)
+  __shared__ __attribute__((aligned(16))) float ks[kBNF32][KP];
+  __shared__ __attribute__((aligned(16))) float vs[kBNF32][D];
+  __shared__ __attribute__((aligned(16))) float qs[kRowsF32][D];
+  __shared__ float ps[kRowsF32][kBNF32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = (int64_t)blockIdx.x / n_qt;
-  const int64_t qi = ((int64_t)blockIdx.x - bh * n_qt) * kRows + t;
+  const int64_t qi = ((int64_t)blockIdx.x - bh * n_qt) * kRowsF32 + w;
   const bool valid = qi < Sq;
   const float* kb = k + bh * Skv * D;
   const float* vb = v + bh * Skv * D;
-
-  float qr[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) qr[d] = valid ? q[(bh * Sq + qi) * D + d] : 0.f;
-#pragma unroll
-  for (int d = 0; d < D; ++d) orun[t][d] = 0.f;
+  for (int e = 0; e < E; ++e) qs[w][lane + 64 * e] = valid ? q[(bh * Sq + qi) * D + lane + 64 * e] : 0.f;
 
   float L = -INFINITY;
-  float acc[D];
+  float o[E], acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
   for (int64_t c0 = 0; c0 < Skv; c0 += chunk) {
     const int64_t c1 = (Skv - c0 < chunk) ? Skv : c0 + chunk;
     float m = -INFINITY, l = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = 0.f;
-    for (int64_t t0 = c0; t0 < c1; t0 += kBN) {
-      const int n = (int)((c1 - t0 < kBN) ? (c1 - t0) : kBN);
-      __syncthreads();
-      for (int e = t; e < kBN * D; e += kRows) {
-        const int j = e / D, d = e - j * D;
-        ks[j][d] = j < n ? kb[(t0 + j) * D + d] : 0.f;
-        vs[j][d] = j < n ? vb[(t0 + j) * D + d] : 0.f;
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int64_t t0 = c0; t0 < c1; t0 += kBNF32) {
+      const int n = (int)((c1 - t0 < kBNF32) ? (c1 - t0) : kBNF32);
+      __syncthreads();  // the previous tile's readers are done (and qs is written)
+      for (int i = tid; i < kBNF32 * (D / 4); i += kThreadsF32) {
+        const int j = i / (D / 4), d4 = (i - j * (D / 4)) * 4;
+        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+        if (j < n) {
+          kx = *reinterpret_cast<const float4*>(kb + (t0 + j) * D + d4);
+          vx = *reinterpret_cast<const float4*>(vb + (t0 + j) * D + d4);
+        }
+        *reinterpret_cast<float4*>(&ks[j][d4]) = kx;
+        *reinterpret_cast<float4*>(&vs[j][d4]) = vx;
       }
       __syncthreads();
-      float s[kBN];
-      float tmax = -INFINITY;
+      // Logit of key `lane` (four partial sums: independent FMA chains).
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kBN; ++j) {
-        float dot = 0.f;
-#pragma unroll
-        for (int d = 0; d < D; ++d) dot = fmaf(qr[d], ks[j][d], dot);
-        s[j] = dot * scale;
-        if (j < n) tmax = fmaxf(tmax, s[j]);
+      for (int d = 0; d < D; d += 4) {
+        const float4 kx = *reinterpret_cast<const float4*>(&ks[lane][d]);
+        const float4 qx = *reinterpret_cast<const float4*>(&qs[w][d]);
+        p4[0] = fmaf(qx.x, kx.x, p4[0]);
+        p4[1] = fmaf(qx.y, kx.y, p4[1]);
+        p4[2] = fmaf(qx.z, kx.z, p4[2]);
+        p4[3] = fmaf(qx.w, kx.w, p4[3]);
       }
-      const float mn = fmaxf(m, tmax);
-      const float alpha = expf(m - mn);  // m = -inf on the first tile: alpha = 0
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] *= alpha;
-#pragma unroll
-      for (int j = 0; j < kBN; ++j) {
-        const float p = j < n ? expf(s[j] - mn) : 0.f;
-        l += p;
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[j][d], acc[d]);
-      }
+      const float s = lane < n ? ((p4[0] + p4[1]) + (p4[2] + p4[3])) * scale : -INFINITY;
+      const float mn = fmaxf(m, wave_max(s));
+      const float alpha = expf(m - mn);  // m = -inf on the chunk's first tile: alpha = 0
+      const float p = lane < n ? expf(s - mn) : 0.f;
+      l = l * alpha + wave_sum(p);
       m = mn;
+      ps[w][lane] = p;
+      __builtin_amdgcn_wave_barrier();  // the wave's own p are written before it reads them
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] *= alpha;
+      for (int j = 0; j < n; ++j) {
+        const float pj = ps[w][j];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(pj, vs[j][lane + 64 * e], acc[e]);
+      }
     }
     // explicit log-sum-exp merge of this chunk into the running result
     const float lse_c = m + logf(l);
@@ -90,7 +114,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
     const float wa = expf(L - Ln);
     const float wb = expf(lse_c - Ln) / l;
 #pragma unroll
-    for (int d = 0; d < D; ++d) orun[t][d] = orun[t][d] * wa + acc[d] * wb;
+    for (int e = 0; e < E; ++e) o[e] = o[e] * wa + acc[e] * wb;
     L = Ln;
   }
   if (valid) {
@@ -98,24 +122,27 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
     const int64_t b = bh / H;
     const int64_t orow = out_bshd ? (b * Sq + qi) * H + (bh - b * H) : bh * Sq + qi;
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[orow * D + d] = orun[t][d];
-    if (lse) lse[bh * Sq + qi] = L;
+    for (int e = 0; e < E; ++e) out[orow * D + lane + 64 * e] = o[e];
+    if (lse && lane == 0) lse[bh * Sq + qi] = L;
   }
 }
 
 }  // namespace
 
+int64_t attn_f32_blocks(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + kRowsF32 - 1) / kRowsF32); }
+int attn_f32_threads() { return kThreadsF32; }
+
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse, int64_t B,
                            int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int64_t kv_chunk,
                            bool out_bshd, hipStream_t stream) {
-  const int64_t n_qt = (Sq + kRows - 1) / kRows;
+  const int64_t n_qt = (Sq + kRowsF32 - 1) / kRowsF32;
   const unsigned grid = (unsigned)(n_qt * B * H);
   if (D == 64)
-    attn_f32_kernel<64><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
-                                                    out_bshd ? 1 : 0);
+    attn_f32_kernel<64><<<grid, kThreadsF32, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
+                                                          out_bshd ? 1 : 0);
   else
-    attn_f32_kernel<128><<<grid, kRows, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
-                                                     out_bshd ? 1 : 0);
+    attn_f32_kernel<128><<<grid, kThreadsF32, 0, stream>>>(q, k, v, out, lse, H, Sq, Skv, scale, kv_chunk, n_qt,
+                                                           out_bshd ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -293,7 +293,8 @@ int check_attn_args(const char* what, const void* q, const void* k, const void* 
   if (!product(nq, {B, H, Sq, D}) || !product(nk, {B, H, Skv, D}) || nq > kMaxElems || nk > kMaxElems)
     return fail(R3D_EINVAL, "%s: tensor too large", what);
   product(bhq, {B, H, Sq});
-  if (dtype == R3D_BF16 ? !r3d::attn_bf16_launches_fit(B, H, Sq) : !launch_fits(B * H * ((Sq + 63) / 64), 64))
+  if (dtype == R3D_BF16 ? !r3d::attn_bf16_launches_fit(B, H, Sq)
+                        : !launch_fits(r3d::attn_f32_blocks(B, H, Sq), r3d::attn_f32_threads()))
     return fail(R3D_EINVAL, "%s: B*H*Sq too large for one launch", what);
   const void* ins[3] = {q, k, v};
   const int64_t in_bytes[3] = {nq * es, nk * es, nk * es};

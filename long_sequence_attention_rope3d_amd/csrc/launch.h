@@ -124,7 +124,10 @@ hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v
                                      float* stats, int* flags, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
                                      int64_t D, float scale, hipStream_t stream);
 
-// attn_fwd, fp32 path (D = 64 or 128); out_bshd as above.
+// attn_fwd, fp32 path (D = 64 or 128); out_bshd as above.  One wave per
+// query row: attn_f32_blocks(B, H, Sq) blocks of attn_f32_threads() threads.
+int64_t attn_f32_blocks(int64_t B, int64_t H, int64_t Sq);
+int attn_f32_threads();
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                            int64_t kv_chunk, bool out_bshd, hipStream_t stream);

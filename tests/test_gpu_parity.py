@@ -559,6 +559,26 @@ def test_attn_random_shapes(gpu, i):
                f"random case {i}")
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_attn_random_shapes_f32(gpu, i):
+    """The fp32 path on seeded random shapes (ragged Sq and Skv, D 64 / 128, kv_chunk 0 or
+    random, scale of either sign), every row against the oracle at the 1e-5 relative bar."""
+    g = np.random.default_rng(9500 + i)
+    D = int(g.choice([64, 128]))
+    B, H = int(g.integers(1, 3)), int(g.integers(1, 5))
+    Sq, Skv = int(g.integers(1, 600)), int(g.integers(1, 2500))
+    kv_chunk = int(g.choice([0, int(g.integers(1, max(2, Skv)))]))
+    scale = float(g.choice([-1.0, 1.0]) * g.uniform(0.02, 0.25))
+    say(f"fp32 case {i}: B={B} H={H} Sq={Sq} Skv={Skv} D={D} kv_chunk={kv_chunk} scale={scale:.4f}")
+    q = _rand((B, H, Sq, D), torch.float32, 500 + 3 * i)
+    k = _rand((B, H, Skv, D), torch.float32, 501 + 3 * i)
+    v = _rand((B, H, Skv, D), torch.float32, 502 + 3 * i)
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
+    check_attn(out, lse, ref_out, ref_lse, torch.float32, f"fp32 case {i}")
+
+
 def test_attn_fwd_without_lse(gpu):
     q = _rand((1, 2, 150, 128), torch.bfloat16, 51).to(gpu)
     k = _rand((1, 2, 190, 128), torch.bfloat16, 52).to(gpu)
