@@ -162,15 +162,17 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  *         keeps there per-head statistics of K and V (2*B*H*64 floats: partial maxima of
  *         |k_j|^2 for a Cauchy-Schwarz bound on every row's logits, and of |v|) and, for
  *         a key-split launch, the fp32 partials (below).
- * Key split: the query tiles (384 rows of one head each) run one block per
- *   tile, a round of blocks per round of the GPU's compute units.  When the
- *   last round would leave many units idle, the tiles of that round instead
- *   run as up to 16 blocks each over ranges of whole chunks (whole 128-key
- *   tiles with one chunk, at least 512 keys), and the ranges' fp32 partials
- *   (O, lse) are merged by the lse_merge kernel into those tiles' rows -- the
- *   ring's per-shard partial + merge, on one device.  A cost model of the
- *   rounds decides (a split must gain 2%).  The result equals the unsplit one
- *   up to rounding.  r3d_attn_fwd_bshd never splits.
+ * Block shape and key split (R3D_BF16): the query tiles (384 rows of one
+ *   head each; for D = 128 a grid of few tiles may use 256-row tiles instead)
+ *   run one block per tile, a round of blocks per round of the GPU's compute
+ *   units.  When the last round would leave many units idle, the tiles of
+ *   that round instead run as up to 16 blocks each over ranges of whole
+ *   chunks (whole 128-key tiles with one chunk, at least 512 keys), and the
+ *   ranges' fp32 partials (O, lse) are merged by the lse_merge kernel into
+ *   those tiles' rows -- the ring's per-shard partial + merge, on one device.
+ *   A cost model of the rounds picks the tile height and the split (either
+ *   must gain 2%).  The result equals that of any other choice up to
+ *   rounding.  r3d_attn_fwd_bshd always uses 384-row tiles and never splits.
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
  * out/lse overlapping an input, a workspace that is NULL, too small, misaligned or
  * overlapping a tensor), R3D_EUNSUPPORTED (D, dtype, or for R3D_BF16 an Sq or Skv
