@@ -7,7 +7,9 @@
  * ---------------------------------------
  *  - Buffers are DEVICE pointers owned by the caller, contiguous (row-major)
  *    in the layout stated per call, 16-byte aligned.  The library allocates
- *    nothing, keeps no pointer after it returns, and creates no stream.
+ *    no device memory at run time (the one fixed array of r3d_attn_fwd_noalloc
+ *    is part of the loaded library), keeps no pointer to caller memory after
+ *    it returns, and creates no stream.
  *    Calls that need device scratch memory take a caller-owned `workspace`
  *    of at least the size their *_workspace_size query reports; its contents
  *    on entry and on return mean nothing to the caller, and it is used in
