@@ -13,9 +13,12 @@
 // 64-key tiles of K and V in LDS.  For a tile, lane j forms key j's logit
 // against the row's query (read from LDS as a broadcast), the wave reduces
 // the tile's max and sum, writes the tile's p to LDS, and lane l accumulates
-// d = l (and l + 64 for D = 128) of P V.  K rows are padded to D + 4 floats
-// so that the 16-byte reads of 16 lanes (16 different rows, same columns)
-// fall into distinct banks; V rows are read along d, conflict-free.
+// d = l (and l + 64 for D = 128) of P V in four interleaved chains.  K rows
+// are padded to D + 4 floats so that the 16-byte reads of 16 lanes (16
+// different rows, same columns) fall into distinct banks; V rows are read
+// along d, conflict-free.  The next tile's K and V are loaded into registers
+// while the current one is computed, so only the first tile's load latency
+// is exposed.
 #include "launch.h"
 
 namespace r3d {
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __re
   __shared__ __attribute__((aligned(16))) float ks[kBNF32][KP];
   __shared__ __attribute__((aligned(16))) float vs[kBNF32][D];
   __shared__ __attribute__((aligned(16))) float qs[kRowsF32][D];
-  __shared__ float ps[kRowsF32][kBNF32];
+  __shared__ __attribute__((aligned(16))) float ps[kRowsF32][kBNF32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = (int64_t)blockIdx.x / n_qt;
   const int64_t qi = ((int64_t)blockIdx.x - bh * n_qt) * kRowsF32 + w;
@@ -57,65 +60,105 @@ __global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __re
 #pragma unroll
   for (int e = 0; e < E; ++e) qs[w][lane + 64 * e] = valid ? q[(bh * Sq + qi) * D + lane + 64 * e] : 0.f;
 
+  // The thread's share of a tile: kLd 16-byte pieces of K and of V, zero past
+  // the tile's n keys.
+  constexpr int kLd = kBNF32 * (D / 4) / kThreadsF32;
+  float4 kn[kLd], vn[kLd];
+  auto fetch = [&](int64_t t0, int n) {
+#pragma unroll
+    for (int r = 0; r < kLd; ++r) {
+      const int i = tid + r * kThreadsF32;
+      const int j = i / (D / 4), d4 = (i - j * (D / 4)) * 4;
+      kn[r] = vn[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < n) {
+        kn[r] = *reinterpret_cast<const float4*>(kb + (t0 + j) * D + d4);
+        vn[r] = *reinterpret_cast<const float4*>(vb + (t0 + j) * D + d4);
+      }
+    }
+  };
+
   float L = -INFINITY;
   float o[E], acc[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
-  for (int64_t c0 = 0; c0 < Skv; c0 += chunk) {
-    const int64_t c1 = (Skv - c0 < chunk) ? Skv : c0 + chunk;
-    float m = -INFINITY, l = 0.f;
+  for (int e = 0; e < E; ++e) o[e] = acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  // Tiles run chunk by chunk: [t0, t0 + n) inside the chunk that ends at c1
+  // (chunk >= 1; the last chunk ends at Skv).
+  int64_t t0 = 0, c1 = chunk < Skv ? chunk : Skv;
+  fetch(0, (int)(c1 < kBNF32 ? c1 : kBNF32));
+  for (;;) {
+    const int n = (int)((c1 - t0 < kBNF32) ? (c1 - t0) : kBNF32);
+    __syncthreads();  // the previous tile's readers are done (and qs is written)
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int64_t t0 = c0; t0 < c1; t0 += kBNF32) {
-      const int n = (int)((c1 - t0 < kBNF32) ? (c1 - t0) : kBNF32);
-      __syncthreads();  // the previous tile's readers are done (and qs is written)
-      for (int i = tid; i < kBNF32 * (D / 4); i += kThreadsF32) {
-        const int j = i / (D / 4), d4 = (i - j * (D / 4)) * 4;
-        float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-        if (j < n) {
-          kx = *reinterpret_cast<const float4*>(kb + (t0 + j) * D + d4);
-          vx = *reinterpret_cast<const float4*>(vb + (t0 + j) * D + d4);
-        }
-        *reinterpret_cast<float4*>(&ks[j][d4]) = kx;
-        *reinterpret_cast<float4*>(&vs[j][d4]) = vx;
-      }
-      __syncthreads();
-      // Logit of key `lane` (four partial sums: independent FMA chains).
-      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < kLd; ++r) {
+      const int i = tid + r * kThreadsF32;
+      const int j = i / (D / 4), d4 = (i - j * (D / 4)) * 4;
+      *reinterpret_cast<float4*>(&ks[j][d4]) = kn[r];
+      *reinterpret_cast<float4*>(&vs[j][d4]) = vn[r];
+    }
+    __syncthreads();
+    const int64_t nt0 = t0 + n;
+    const bool chunk_end = nt0 >= c1;
+    const int64_t nc1 = chunk_end ? ((Skv - c1 < chunk) ? Skv : c1 + chunk) : c1;
+    const bool more = nt0 < Skv;
+    if (more) fetch(nt0, (int)((nc1 - nt0 < kBNF32) ? (nc1 - nt0) : kBNF32));
+
+    // Logit of key `lane` (four partial sums: independent FMA chains).
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < D; d += 4) {
-        const float4 kx = *reinterpret_cast<const float4*>(&ks[lane][d]);
-        const float4 qx = *reinterpret_cast<const float4*>(&qs[w][d]);
-        p4[0] = fmaf(qx.x, kx.x, p4[0]);
-        p4[1] = fmaf(qx.y, kx.y, p4[1]);
-        p4[2] = fmaf(qx.z, kx.z, p4[2]);
-        p4[3] = fmaf(qx.w, kx.w, p4[3]);
-      }
-      const float s = lane < n ? ((p4[0] + p4[1]) + (p4[2] + p4[3])) * scale : -INFINITY;
-      const float mn = fmaxf(m, wave_max(s));
-      const float alpha = expf(m - mn);  // m = -inf on the chunk's first tile: alpha = 0
-      const float p = lane < n ? expf(s - mn) : 0.f;
-      l = l * alpha + wave_sum(p);
-      m = mn;
-      ps[w][lane] = p;
-      __builtin_amdgcn_wave_barrier();  // the wave's own p are written before it reads them
+    for (int d = 0; d < D; d += 4) {
+      const float4 kx = *reinterpret_cast<const float4*>(&ks[lane][d]);
+      const float4 qx = *reinterpret_cast<const float4*>(&qs[w][d]);
+      p4[0] = fmaf(qx.x, kx.x, p4[0]);
+      p4[1] = fmaf(qx.y, kx.y, p4[1]);
+      p4[2] = fmaf(qx.z, kx.z, p4[2]);
+      p4[3] = fmaf(qx.w, kx.w, p4[3]);
+    }
+    const float s = lane < n ? ((p4[0] + p4[1]) + (p4[2] + p4[3])) * scale : -INFINITY;
+    const float mn = fmaxf(m, wave_max(s));
+    const float alpha = expf(m - mn);  // m = -inf on the chunk's first tile: alpha = 0
+    const float p = lane < n ? expf(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+    m = mn;
+    ps[w][lane] = p;
+    __builtin_amdgcn_wave_barrier();  // the wave's own p are written before it reads them
+    // P V over all 64 keys of the tile: keys past n have p = 0 and zero V rows.
+    float a4[E][4];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] *= alpha;
-      for (int j = 0; j < n; ++j) {
-        const float pj = ps[w][j];
+    for (int e = 0; e < E; ++e) a4[e][0] = a4[e][1] = a4[e][2] = a4[e][3] = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(pj, vs[j][lane + 64 * e], acc[e]);
+    for (int j = 0; j < kBNF32; j += 4) {
+      const float4 pj = *reinterpret_cast<const float4*>(&ps[w][j]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        a4[e][0] = fmaf(pj.x, vs[j][lane + 64 * e], a4[e][0]);
+        a4[e][1] = fmaf(pj.y, vs[j + 1][lane + 64 * e], a4[e][1]);
+        a4[e][2] = fmaf(pj.z, vs[j + 2][lane + 64 * e], a4[e][2]);
+        a4[e][3] = fmaf(pj.w, vs[j + 3][lane + 64 * e], a4[e][3]);
       }
     }
-    // explicit log-sum-exp merge of this chunk into the running result
-    const float lse_c = m + logf(l);
-    const float hi = fmaxf(L, lse_c);
-    const float Ln = (L == -INFINITY) ? lse_c : hi + logf(expf(L - hi) + expf(lse_c - hi));
-    const float wa = expf(L - Ln);
-    const float wb = expf(lse_c - Ln) / l;
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = o[e] * wa + acc[e] * wb;
-    L = Ln;
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(acc[e], alpha, (a4[e][0] + a4[e][1]) + (a4[e][2] + a4[e][3]));
+
+    if (chunk_end) {
+      // explicit log-sum-exp merge of this chunk into the running result
+      const float lse_c = m + logf(l);
+      const float hi = fmaxf(L, lse_c);
+      const float Ln = (L == -INFINITY) ? lse_c : hi + logf(expf(L - hi) + expf(lse_c - hi));
+      const float wa = expf(L - Ln);
+      const float wb = expf(lse_c - Ln) / l;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        o[e] = o[e] * wa + acc[e] * wb;
+        acc[e] = 0.f;
+      }
+      L = Ln;
+      m = -INFINITY;
+      l = 0.f;
+    }
+    if (!more) break;
+    t0 = nt0;
+    c1 = nc1;
   }
   if (valid) {
     // out row of (b, h, qi): [B, H, Sq, D], or [B, Sq, H, D] (token-major).
