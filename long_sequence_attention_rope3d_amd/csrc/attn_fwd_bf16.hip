@@ -126,7 +126,7 @@ constexpr int kBN = R3D_ATTN_BN;  // keys per LDS tile (a multiple of 32)
 static_assert(kAttnMaxSeq + kBN <= INT32_MAX, "key cursor fits in 32 bits");
 constexpr int kSub = kBN / 32;   // 32-key softmax steps per tile
 constexpr int kXcds = 8;
-constexpr int kSlackMax = 64;     // largest bound slack under which the row max is skipped, log2 units
+constexpr int kSlackMax = 32;     // largest bound slack under which the row max is skipped, log2 units
 
 template <int D, int W>
 struct Geom {
@@ -301,11 +301,11 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // The slack is per head: the accumulator sums up to chunk + 1 terms of
 // p |v| (the chunk's keys and the carried result), so the slack is capped
 // at E = 126 - ceil(log2(chunk + 1)) - floor(log2(max |v|)), which keeps
-// |acc| below 2^127 (fp32 ends at 2^128): min(64, E).  Where even p <= 1
+// |acc| below 2^127 (fp32 ends at 2^128): min(32, E).  Where even p <= 1
 // would not (E < 0: |v| near the top of bf16's range), the reference is held
 // `off` = -E above the row's max -- a moved reference is max + off, a carried
 // chunk result enters at weight 2^-off -- so every p <= 2^E.  For ordinary
-// inputs E >= 64 and off = 0.  Either way the reference only sets the scale
+// inputs E >= 32 and off = 0.  Either way the reference only sets the scale
 // of acc and l: the result is the online softmax's for every finite input,
 // without its overflow for very large V.
 //
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(Blk<W>::kThreads, Blk<W>::kWavesPerSimd) void attn_
     vabs_max = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b)));
   }
   // Per-head slack and reference offset (see the kernel's comment):
-  // E = 126 - chunk_bits - floor(log2 max|v|), slack = min(64, E),
+  // E = 126 - chunk_bits - floor(log2 max|v|), slack = min(32, E),
   // off = max(0, -E); a non-finite V (exponent field 255) keeps the plain
   // online softmax's p <= 1.
   float slack, off, carry;

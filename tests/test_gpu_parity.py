@@ -384,19 +384,18 @@ def test_attn_fwd_small(gpu, case):
 
 
 @pytest.mark.parametrize("D,gap,kv_chunk", [
-    (128, 28.0, 0), (128, 28.0, 256), (128, 60.0, 0), (128, 60.0, 300), (128, 72.0, 0),
-    (128, 72.0, 300), (128, 0.0, 300), (64, 28.0, 128), (64, 62.0, 0), (64, 80.0, 0),
+    (128, 28.0, 0), (128, 28.0, 256), (128, 40.0, 0), (128, 40.0, 300), (128, 0.0, 300),
+    (64, 28.0, 128), (64, 45.0, 0),
 ])
 def test_attn_bound_gated_max(gpu, D, gap, kv_chunk):
     """The bf16 kernel forms a row's max only while the row's Cauchy-Schwarz bound
-    c |q| max_j |k_j| exceeds its reference by more than the head's slack (64 in log2 units
-    for these V and chunk lengths).  Half of the rows point along one direction u with
-    |q| = 10; key 3 is b1*u and key 700 is b2*u, so those rows' reference after the first
-    step is c*10*b1 and their bound is c*10*b2, `gap` log2 units higher.  gap 28 and 60: the
-    max is skipped and key 700 arrives with p ~ 2^gap; gap 72 and 80: the max is formed and
-    the reference moves at key 700; gap 0: the bound is attained at key 3.  The other rows
-    (|q| ~ 0.3, random direction) sit in the other regime in the same waves.  Every case must
-    match the oracle."""
+    c |q| max_j |k_j| exceeds its reference by more than a fixed slack (32 in log2 units).
+    Half of the rows point along one direction u with |q| = 10; key 3 is b1*u and key 700 is
+    b2*u, so those rows' reference after the first step is c*10*b1 and their bound is
+    c*10*b2, `gap` log2 units higher.  gap 28: the max is skipped and key 700 arrives with
+    p ~ 2^28; gap 40: the max is formed and the reference moves at key 700; gap 0: the bound
+    is attained at key 3.  The other rows (|q| ~ 0.3, random direction) sit in the other
+    regime in the same waves.  Every case must match the oracle."""
     B, H, Sq, Skv = 1, 2, 200, 1000
     scale = 1.0 / math.sqrt(D)
     c = scale / math.log(2.0)
@@ -425,8 +424,8 @@ def test_attn_bound_gated_max(gpu, D, gap, kv_chunk):
 ])
 def test_attn_gated_max_large_v(gpu, D, gap, kv_chunk, vexp):
     """The gap construction of test_attn_bound_gated_max with V scaled by 2^vexp (exact in
-    bf16).  With a fixed slack of 28 or more, key 700 would enter with p ~ 2^28 and
-    |p v| ~ 2^133 would overflow fp32.  The kernel caps each head's slack at
+    bf16).  With the slack fixed at 32, key 700 would enter with p ~ 2^28 and |p v| ~ 2^133
+    would overflow fp32.  The kernel caps each head's slack at
     126 - ceil(log2(chunk + 1)) - floor(log2 max|v|) (2^103: slack 13-16), and past the point
     where even p <= 1 would overflow (2^125 with ~1000-key chunks) holds the reference
     above the row max so every p <= 2^(that cap).  Attention is linear in V, so out / 2^vexp
