@@ -1,0 +1,70 @@
+"""The entry points run in order on the caller's stream (torch's current stream, passed
+through the C ABI), not on the null stream.
+
+Each case makes a side stream spin for ~20 ms (torch.cuda._sleep), then writes the
+call's input on that stream and calls the entry point under it.  A launch on any other
+stream would read the input before the write lands; on the caller's stream it must see
+the written input, and its result must still be pending when the host returns (the
+spin is still running).  The result is then compared bit for bit with the same call
+made on the default stream with nothing pending.
+"""
+import pytest
+import torch
+
+import long_sequence_attention_rope3d_amd as r3d
+
+pytestmark = pytest.mark.gpu
+
+SPIN = 40_000_000  # shader clock cycles: ~20 ms
+
+
+def _rand(shape, seed, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype)
+
+
+def test_attn_fwd_runs_on_the_current_stream(gpu):
+    q, k, v = (_rand((1, 3, 700, 128), s).to(gpu) for s in (1, 2, 3))
+    want, want_lse = r3d.attn_fwd(q, k, v, kv_chunk=256)
+    torch.cuda.synchronize()
+    q_in = torch.zeros_like(q)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN)
+        q_in.copy_(q)
+        out, lse = r3d.attn_fwd(q_in, k, v, kv_chunk=256)
+    assert not side.query(), "the call's work should still be queued behind the spin"
+    side.synchronize()
+    assert torch.equal(out, want) and torch.equal(lse, want_lse)
+
+
+def test_joint_concat_permute_runs_on_the_current_stream(gpu):
+    segs = [_rand((1, n, 4, 128), 10 + i).to(gpu) for i, n in enumerate((24, 7))]
+    rope = r3d.Rope3D((2, 3, 4), (32, 48, 48))
+    want = r3d.joint_concat_permute(segs, rope)
+    torch.cuda.synchronize()
+    seg0 = torch.zeros_like(segs[0])
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN)
+        seg0.copy_(segs[0])
+        out = r3d.joint_concat_permute([seg0, segs[1]], rope)
+    assert not side.query()
+    side.synchronize()
+    assert torch.equal(out, want)
+
+
+def test_lse_merge_runs_on_the_current_stream(gpu):
+    parts = _rand((3, 1, 2, 300, 64), 20, torch.float32).to(gpu)
+    lses = _rand((3, 1, 2, 300), 21, torch.float32).to(gpu)
+    want, want_lse = r3d.lse_merge(parts, lses)
+    torch.cuda.synchronize()
+    parts_in = torch.zeros_like(parts)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(SPIN)
+        parts_in.copy_(parts)
+        out, lse = r3d.lse_merge(parts_in, lses)
+    assert not side.query()
+    side.synchronize()
+    assert torch.equal(out, want) and torch.equal(lse, want_lse)
