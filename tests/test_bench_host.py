@@ -58,3 +58,12 @@ def test_mfma_counters_follow_the_kernel_hash(tmp_path, monkeypatch):
     src.write_text("int f() { return 2; }\n")
     assert b._mfma_counters_for_current_kernel() is None
 
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    """bench.py --gpus N with N != 1 exits with status 2 and says why (one GPU only)."""
+    import subprocess
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert p.returncode == 2
+    assert "exactly one GPU" in (p.stdout + p.stderr)
