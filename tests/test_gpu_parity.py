@@ -579,6 +579,31 @@ def test_attn_random_shapes_f32(gpu, i):
     check_attn(out, lse, ref_out, ref_lse, torch.float32, f"fp32 case {i}")
 
 
+@pytest.mark.parametrize("dtype,kv_chunk", [(torch.bfloat16, 0), (torch.bfloat16, 64), (torch.float32, 64)])
+def test_attn_nan_inputs_propagate_like_the_oracle(gpu, dtype, kv_chunk):
+    """A NaN in one key of head 1 makes every row of that head NaN (that key is in every row's
+    softmax); a NaN in one query row of head 2 makes only that row NaN; the oracle agrees on every
+    element, and the finite rows meet the usual bar."""
+    B, H, Sq, Skv, D = 1, 3, 200, 300, 128
+    q = _rand((B, H, Sq, D), dtype, 71)
+    k = _rand((B, H, Skv, D), dtype, 72)
+    v = _rand((B, H, Skv, D), dtype, 73)
+    k[0, 1, 57, 3] = float("nan")
+    q[0, 2, 10, 5] = float("nan")
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(D))
+    got_out = to_f64(out.cpu())
+    got_lse = lse.cpu().double().numpy()
+    assert np.array_equal(np.isnan(got_out), np.isnan(ref_out))
+    assert np.array_equal(np.isnan(got_lse), np.isnan(ref_lse))
+    assert np.isnan(ref_out[0, 1]).all() and np.isnan(ref_out[0, 2, 10]).all()
+    assert not np.isnan(ref_out[0, 0]).any() and not np.isnan(np.delete(ref_out[0, 2], 10, axis=0)).any()
+    keep = ~np.isnan(ref_lse)
+    check_attn(torch.from_numpy(got_out[keep]), torch.from_numpy(got_lse[keep]), ref_out[keep], ref_lse[keep], dtype,
+               f"NaN inputs {dtype} kv_chunk={kv_chunk}, finite rows")
+
+
 def test_attn_fwd_without_lse(gpu):
     q = _rand((1, 2, 150, 128), torch.bfloat16, 51).to(gpu)
     k = _rand((1, 2, 190, 128), torch.bfloat16, 52).to(gpu)
