@@ -306,8 +306,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // `off` = -E above the row's max -- a moved reference is max + off, a carried
 // chunk result enters at weight 2^-off -- so every p <= 2^E.  For ordinary
 // inputs E >= 32 and off = 0.  Either way the reference only sets the scale
-// of acc and l: the result is the online softmax's for every finite input,
-// without its overflow for very large V.
+// of acc and l: the result is the online softmax's for every finite input up
+// to the bf16 rounding of p (a key above a skipped max enters with p > 1,
+// rounded like any p, where the online softmax gives it exactly 1), without
+// its overflow for very large V.
 //
 // kConstMax: the reference is the bound itself, fixed before any key is read:
 // no max reduction, no rescale, and chunk partials simply add.  Exact as long
