@@ -47,6 +47,7 @@ MI355X_HBM_GBPS = 8000.0
 METRIC = "attention TFLOP/s (4·B·H·Sq·Skv·D) + % bf16 MFMA peak; ms/call at 52k tokens"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_traffic.md")
 MFMA_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_mfma_util.md")
+POWER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_pro-clip_power.md")
 ATTN_SRC = os.path.join(ROOT, "long_sequence_attention_rope3d_amd", "csrc", "attn_fwd_bf16.hip")
 
 
@@ -100,6 +101,11 @@ def _mfma_counters_for_current_kernel():
     if vals is None:
         return None
     vals["source"] = os.path.relpath(MFMA_FILE, ROOT)
+    # Board power under the same kernel (SMI samples beside the bench loop), if recorded.
+    power = _profile_values(POWER_FILE, ["package_power_w_under_load", "power_cap_w"])
+    if power is not None:
+        vals.update(power)
+        vals["power_source"] = os.path.relpath(POWER_FILE, ROOT)
     return vals
 
 

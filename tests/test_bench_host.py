@@ -67,3 +67,22 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
                        text=True, timeout=300)
     assert p.returncode == 2
     assert "exactly one GPU" in (p.stdout + p.stderr)
+
+
+def test_power_figures_follow_the_kernel_hash(tmp_path, monkeypatch):
+    b = _bench()
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }\n")
+    h = b.kernel_code_sha256(str(src))
+    mfma = tmp_path / "mfma.md"
+    mfma.write_text(f"kernel_code_sha256: {h}\nmfma_busy_frac: 0.67\nsclk_ghz_under_load: 1.77\n")
+    power = tmp_path / "power.md"
+    power.write_text(f"kernel_code_sha256: {h}\npackage_power_w_under_load: 1349\npower_cap_w: 1400\n")
+    monkeypatch.setattr(b, "ATTN_SRC", str(src))
+    monkeypatch.setattr(b, "MFMA_FILE", str(mfma))
+    monkeypatch.setattr(b, "POWER_FILE", str(power))
+    c = b._mfma_counters_for_current_kernel()
+    assert c["package_power_w_under_load"] == 1349 and c["power_cap_w"] == 1400
+    power.write_text("kernel_code_sha256: " + "0" * 64 + "\npackage_power_w_under_load: 1349\npower_cap_w: 1400\n")
+    c = b._mfma_counters_for_current_kernel()
+    assert "package_power_w_under_load" not in c and c["mfma_busy_frac"] == 0.67
