@@ -207,3 +207,40 @@ def test_lse_merge_past_2g_elements(gpu):
     assert (dl <= 1e-5 * np.maximum(1.0, np.abs(ref_lse))).all()
     del parts, lse_parts, out, lse
     torch.cuda.empty_cache()
+
+
+def test_rope3d_apply_in_place_past_2g_elements(gpu):
+    """rope3d_apply in place on [1, 999424, 17, 128] bf16 video tokens (2.18e9 elements, grid
+    61x128x128): sampled (token, head) rows on both sides of element 2^31 and at the ends equal
+    the oracle's rotation of the saved input rows, rounded to bf16 (within 1 ulp, >= 99.9% equal)."""
+    grid, split, theta = (61, 128, 128), (32, 48, 48), 10000.0
+    H, D = 17, 128
+    Nv = grid[0] * grid[1] * grid[2]
+    assert Nv * H * D > I31
+    say(f"large rope3d_apply in place: grid={grid} H={H} D={D}")
+    x = _randn((1, Nv, H, D), 71, gpu)
+    cross = I31 // D                       # flat (token, head) row holding element 2^31
+    pairs = {divmod(cross + d, H) for d in (-1, 0, 1)}
+    pairs |= {(0, 0), (Nv - 1, H - 1), (Nv // 2, 3)}
+    rng = np.random.default_rng(71)
+    pairs |= {(int(s), int(h)) for s, h in zip(rng.integers(0, Nv, 24), rng.integers(0, H, 24))}
+    pairs = sorted(pairs)
+    saved = [to_f64(x[0, s, h].cpu()) for s, h in pairs]
+    y = r3d.rope3d_apply(x, grid, split, theta, out=x)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr()
+    got = np.array([to_f64(x[0, s, h].cpu()) for s, h in pairs])
+    ref = []
+    for (s, h), v in zip(pairs, saved):
+        t, rem = divmod(s, grid[1] * grid[2])
+        hh, w = divmod(rem, grid[2])
+        ref.append(oracle.round_bf16(oracle.rope_vec(v, (t, hh, w), split, theta)))
+    ref = np.array(ref)
+    d = np.abs(got - ref)
+    ax = np.abs(ref)
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(ax > 0, ax, 1.0))), -126) - 7)
+    say(f"[rope3d_apply past 2^31] {len(pairs)} rows: exact fraction {(d == 0).mean():.6f}, "
+        f"max ulps {(d / ulp).max():.2f}")
+    assert (d <= ulp).all() and (d == 0).mean() >= 0.999
+    del x
+    torch.cuda.empty_cache()
