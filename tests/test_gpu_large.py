@@ -244,3 +244,55 @@ def test_rope3d_apply_in_place_past_2g_elements(gpu):
     assert (d <= ulp).all() and (d == 0).mean() >= 0.999
     del x
     torch.cuda.empty_cache()
+
+
+def test_permute_qknorm_rope_past_2g_elements(gpu):
+    """joint_concat_permute with the RMS QK-norm (weights on the video and text segments) and
+    RoPE, 2.18e9 elements (the 61x128x128 video grid + 256 audio + 512 text tokens, 17 heads x
+    128): sampled tokens on both sides of each 2^31 crossing against the oracle's norm over the
+    token's H*D values (stored in bf16), then its rotation (stored in bf16); within 1 ulp and
+    >= 99.9% equal; the audio segment (no weights) bit-exact."""
+    grid, split, theta, eps = (61, 128, 128), (32, 48, 48), 10000.0, 1e-6
+    H, D = 17, 128
+    Nv = grid[0] * grid[1] * grid[2]
+    lens = (Nv, 256, 512)
+    S = sum(lens)
+    assert H * S * D > I31
+    say(f"large permute + QK-norm + RoPE: grid={grid} lens={lens} H={H} D={D}")
+    segs = [_randn((1, n, H, D), 81 + i, gpu) for i, n in enumerate(lens)]
+    g = torch.Generator().manual_seed(81)
+    wts = [1.0 + 0.3 * torch.randn(H * D, generator=g), None, 0.5 + torch.rand(H * D, generator=g)]
+    out = r3d.joint_concat_permute(segs, r3d.Rope3D(grid, split, theta),
+                                   norm=[w.to(gpu) if w is not None else None for w in wts], eps=eps)
+    torch.cuda.synchronize()
+    dst_cross = I31 // D                    # h*S + s of destination element 2^31
+    src_cross = I31 // D // H               # video token holding source element 2^31
+    toks = {dst_cross % S + d for d in (-1, 0, 1)} | {src_cross + d for d in (-1, 0, 1)}
+    toks |= {0, Nv - 1, Nv, Nv + 255, Nv + 256, S - 1}
+    rng = np.random.default_rng(81)
+    toks |= {int(s) for s in rng.integers(0, S, 12)}
+    offs = np.cumsum((0,) + lens)
+    got, ref, exact_seg = [], [], []
+    for s in sorted(toks):
+        seg = int(np.searchsorted(offs, s, side="right")) - 1
+        x = to_f64(segs[seg][0, s - offs[seg]].cpu())          # [H, D]: the whole token
+        y = x
+        if wts[seg] is not None:
+            y = oracle.round_bf16(oracle.rms_norm(x.reshape(1, H * D), wts[seg].double().numpy(), eps)).reshape(H, D)
+        if seg == 0:
+            t, rem = divmod(s, grid[1] * grid[2])
+            hh, w = divmod(rem, grid[2])
+            y = np.stack([oracle.round_bf16(oracle.rope_vec(y[h], (t, hh, w), split, theta)) for h in range(H)])
+        got.append(to_f64(out[0, :, s].cpu()))
+        ref.append(y)
+        exact_seg.append(wts[seg] is None and seg != 0)
+    got, ref = np.array(got), np.array(ref)
+    d = np.abs(got - ref)
+    ax = np.abs(ref)
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(ax > 0, ax, 1.0))), -126) - 7)
+    say(f"[QK-norm past 2^31] {len(toks)} tokens x {H} heads: exact fraction {(d == 0).mean():.6f}, "
+        f"max ulps {(d / ulp).max():.2f}")
+    assert (d[np.array(exact_seg)] == 0).all()
+    assert (d <= ulp).all() and (d == 0).mean() >= 0.999
+    del segs, out
+    torch.cuda.empty_cache()
