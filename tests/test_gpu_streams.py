@@ -1,7 +1,7 @@
 """The entry points run in order on the caller's stream (torch's current stream, passed
 through the C ABI), not on the null stream.
 
-Each case makes a side stream spin for ~20 ms (torch.cuda._sleep), then writes the
+Each case makes a side stream spin for ~0.2 s (torch.cuda._sleep), then writes the
 call's input on that stream and calls the entry point under it.  A launch on any other
 stream would read the input before the write lands; on the caller's stream it must see
 the written input, and its result must still be pending when the host returns (the
@@ -15,7 +15,7 @@ import long_sequence_attention_rope3d_amd as r3d
 
 pytestmark = pytest.mark.gpu
 
-SPIN = 40_000_000  # shader clock cycles: ~20 ms
+SPIN = 400_000_000  # shader clock cycles: ~0.2 s, far longer than the host needs to enqueue and query
 
 
 def _rand(shape, seed, dtype=torch.bfloat16):
