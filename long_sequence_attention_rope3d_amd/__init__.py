@@ -25,6 +25,7 @@ allocator, in the call's stream order).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -138,6 +139,23 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _one_device(first: torch.Tensor, first_name: str, **others: Optional[torch.Tensor]) -> torch.device:
+    """The device of ``first``; every other tensor given must be on it.  The
+    library plans and launches on the current device, so each call runs with
+    this device made current (_on)."""
+    if not isinstance(first, torch.Tensor) or not first.is_cuda:
+        raise ValueError(f"{first_name} must be a GPU tensor (got {getattr(first, 'device', type(first))})")
+    for name, t in others.items():
+        if t is not None and isinstance(t, torch.Tensor) and t.device != first.device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors on {first.device}")
+    return first.device
+
+
+def _on(dev: torch.device):
+    """Context making ``dev`` the current device; free when it already is (the usual case)."""
+    return contextlib.nullcontext() if dev.index == torch.cuda.current_device() else torch.cuda.device(dev)
+
+
 def rope3d_apply(x: torch.Tensor, grid, split, theta: float = 10000.0,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Rotate video tokens x [B, Nv, H, D] by their (t, h, w) grid position.
@@ -150,8 +168,9 @@ def rope3d_apply(x: torch.Tensor, grid, split, theta: float = 10000.0,
         raise ValueError("out must match x in shape and dtype")
     B, Nv, H, D = x.shape
     desc = Rope3D(tuple(grid), tuple(split), theta).desc()
-    _check(_lib.r3d_rope3d_apply(_dev(x, "x"), _dev(out, "out"), _dtype_code(x), B, Nv, H, D,
-                                 ctypes.byref(desc), _stream(x)), "rope3d_apply")
+    with _on(_one_device(x, "x", out=out)):
+        _check(_lib.r3d_rope3d_apply(_dev(x, "x"), _dev(out, "out"), _dtype_code(x), B, Nv, H, D,
+                                     ctypes.byref(desc), _stream(x)), "rope3d_apply")
     return out
 
 
@@ -179,16 +198,18 @@ def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = 
         out = torch.empty((B, H, S, D), dtype=dt, device=segs[0].device)
     if tuple(out.shape) != (B, H, S, D) or out.dtype != dt:
         raise ValueError("out must be [B, H, S, D] of the segments' dtype")
+    dev = _one_device(segs[0], "segment", out=out)
     ptrs = (ctypes.c_void_p * len(segs))(
         *[(_dev(s, "segment") if s.shape[1] > 0 else None) for s in segs])
     lens = (ctypes.c_int64 * len(segs))(*[int(s.shape[1]) for s in segs])
     desc = rope.desc() if rope is not None else None
     rope_arg = ctypes.byref(desc) if desc is not None else None
     if norm is None:
-        _check(_lib.r3d_joint_concat_permute(ctypes.cast(ptrs, ctypes.c_void_p),
-                                             ctypes.cast(lens, ctypes.c_void_p), len(segs),
-                                             _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
-                                             _stream(out)), "joint_concat_permute")
+        with _on(dev):
+            _check(_lib.r3d_joint_concat_permute(ctypes.cast(ptrs, ctypes.c_void_p),
+                                                 ctypes.cast(lens, ctypes.c_void_p), len(segs),
+                                                 _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
+                                                 _stream(out)), "joint_concat_permute")
         return out
     norm = list(norm)
     if len(norm) != len(segs):
@@ -196,13 +217,15 @@ def joint_concat_permute(segs: Sequence[torch.Tensor], rope: Optional[Rope3D] = 
     for w in norm:
         if w is not None and (w.dtype != torch.float32 or w.numel() != H * D or not w.is_contiguous()):
             raise ValueError("norm weights must be contiguous float32 vectors of H*D values")
+        _one_device(segs[0], "segment", norm_weight=w)
     wptrs = (ctypes.c_void_p * len(segs))(*[(_dev(w, "norm weight") if w is not None else None)
                                              for w in norm])
-    _check(_lib.r3d_joint_concat_permute_qknorm(ctypes.cast(ptrs, ctypes.c_void_p),
-                                                ctypes.cast(lens, ctypes.c_void_p), len(segs),
-                                                ctypes.cast(wptrs, ctypes.c_void_p), float(eps),
-                                                _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
-                                                _stream(out)), "joint_concat_permute_qknorm")
+    with _on(dev):
+        _check(_lib.r3d_joint_concat_permute_qknorm(ctypes.cast(ptrs, ctypes.c_void_p),
+                                                    ctypes.cast(lens, ctypes.c_void_p), len(segs),
+                                                    ctypes.cast(wptrs, ctypes.c_void_p), float(eps),
+                                                    _dev(out, "out"), _dtype_code(out), B, H, D, rope_arg,
+                                                    _stream(out)), "joint_concat_permute_qknorm")
     return out
 
 
@@ -266,11 +289,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
     fn = _lib.r3d_attn_fwd if out_layout == "bhsd" else _lib.r3d_attn_fwd_bshd
-    need = attn_fwd_workspace_size(B, H, Sq, Skv, D, int(kv_chunk), q.dtype) if workspace is None else 0
-    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
-    _check(fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-              _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
-              float(scale), int(kv_chunk), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)), "attn_fwd")
+    with _on(_one_device(q, "q", k=k, v=v, out=out, lse=lse, workspace=workspace)):
+        need = attn_fwd_workspace_size(B, H, Sq, Skv, D, int(kv_chunk), q.dtype) if workspace is None else 0
+        ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
+        _check(fn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                  _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                  float(scale), int(kv_chunk), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)), "attn_fwd")
     return (out, lse) if lse is not None else out
 
 
@@ -298,9 +322,11 @@ def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: O
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
-    _check(_lib.r3d_attn_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                     _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
-                                     float(scale), int(kv_chunk), _dtype_code(q), _stream(q)), "attn_fwd_noalloc")
+    with _on(_one_device(q, "q", k=k, v=v, out=out, lse=lse)):
+        _check(_lib.r3d_attn_fwd_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                         _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                                         float(scale), int(kv_chunk), _dtype_code(q), _stream(q)),
+               "attn_fwd_noalloc")
     return (out, lse) if lse is not None else out
 
 
@@ -330,12 +356,13 @@ def attn_fwd_constmax(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if lse is not None and (tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32):
         raise ValueError("lse must be [B, H, Sq] float32")
-    need = attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, q.dtype) if workspace is None else 0
-    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
-    _check(_lib.r3d_attn_fwd_constmax(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                      _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
-                                      float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)),
-           "attn_fwd_constmax")
+    with _on(_one_device(q, "q", k=k, v=v, out=out, lse=lse, workspace=workspace)):
+        need = attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, q.dtype) if workspace is None else 0
+        ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
+        _check(_lib.r3d_attn_fwd_constmax(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                          _dev(lse, "lse") if lse is not None else None, B, H, Sq, Skv, D,
+                                          float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream(q)),
+               "attn_fwd_constmax")
     return (out, lse) if lse is not None else out
 
 
@@ -355,10 +382,13 @@ def lse_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, out_dtype: Optiona
         raise ValueError("out must be [B, H, S, D]")
     if lse_out is None and return_lse:
         lse_out = torch.empty((B, H, S), dtype=torch.float32, device=o_parts.device)
-    _check(_lib.r3d_lse_merge(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n,
-                              _dtype_code(o_parts), _dev(out, "out"),
-                              _dev(lse_out, "lse_out") if lse_out is not None else None,
-                              _dtype_code(out), B, H, S, D, _stream(out)), "lse_merge")
+    if lse_out is not None and (tuple(lse_out.shape) != (B, H, S) or lse_out.dtype != torch.float32):
+        raise ValueError("lse_out must be [B, H, S] float32")
+    with _on(_one_device(o_parts, "o_parts", lse_parts=lse_parts, out=out, lse_out=lse_out)):
+        _check(_lib.r3d_lse_merge(_dev(o_parts, "o_parts"), _dev(lse_parts, "lse_parts"), n,
+                                  _dtype_code(o_parts), _dev(out, "out"),
+                                  _dev(lse_out, "lse_out") if lse_out is not None else None,
+                                  _dtype_code(out), B, H, S, D, _stream(out)), "lse_merge")
     return (out, lse_out) if lse_out is not None else out
 
 

@@ -917,3 +917,23 @@ def test_attn_constmax_outlier_gate(gpu):
     idx = torch.from_numpy(rows).to(gpu)
     check_attn(out.reshape(-1, w.D)[idx], lse.reshape(-1)[idx], ref_out, ref_lse, out.dtype,
                "constmax long-video (flagged tiles recomputed)")
+
+
+def test_binding_rejects_mixed_devices_and_bad_lse_out(gpu):
+    """Every tensor of a call must be on the first one's device (the call runs
+    with that device current); lse_merge checks a given lse_out like out.  Both
+    are refused before any launch, and nothing the caller passed is written."""
+    q = _rand((1, 2, 64, 64), torch.bfloat16, 1).to(gpu)
+    with pytest.raises(ValueError, match="k is on cpu"):
+        r3d.attn_fwd(q, q.cpu(), q)
+    with pytest.raises(ValueError, match="out is on cpu"):
+        r3d.rope3d_apply(q.transpose(1, 2).contiguous(), (1, 8, 8), (16, 24, 24), out=torch.empty(1, 64, 2, 64, dtype=torch.bfloat16))
+    parts = _rand((3, 1, 2, 64, 64), torch.float32, 2).to(gpu)
+    lses = _rand((3, 1, 2, 64), torch.float32, 3).to(gpu)
+    small = torch.full((1, 2, 32), 7.0, device=gpu)
+    with pytest.raises(ValueError, match="lse_out must be"):
+        r3d.lse_merge(parts, lses, lse_out=small)
+    with pytest.raises(ValueError, match="lse_out must be"):
+        r3d.lse_merge(parts, lses, lse_out=torch.empty((1, 2, 64), dtype=torch.bfloat16, device=gpu))
+    torch.cuda.synchronize()
+    assert bool((small == 7.0).all())
