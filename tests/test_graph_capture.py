@@ -78,3 +78,38 @@ def test_permute_and_merge_graph_replay(gpu):
         r3d.joint_concat_permute(segs, rope, norm=wts, eps=1e-6, out=out_p)
         r3d.lse_merge(parts, lp, out=out_m, lse_out=out_l)
     _replay_and_check(g, [out_p, out_m, out_l], [want_p, want_m, want_l], lambda: None)
+
+
+def test_attn_constmax_graph_replay(gpu):
+    """The constant-max call records three kernels (pre-pass, constant-max pass, recompute
+    of flagged tiles); the flags live in the workspace.  One key of heads 0 and 2 is scaled
+    x64, so their bound overshoots most rows' maxima past fp32's range and those tiles are
+    recomputed, while heads 1 and 3 are not.  Between replays an eager call on inputs
+    without the outlier rewrites the workspace's statistics and flags."""
+    B, H, Sq, Skv, D = 1, 4, 900, 1500, 128
+    q, k, v = (_rand((B, H, S, D), torch.bfloat16, 90 + i).to(gpu) for i, S in enumerate((Sq, Skv, Skv)))
+    k_plain = k.clone()
+    k[:, 0::2, 7, :] *= 64
+    scale = 1.0 / math.sqrt(D)
+    ws = torch.empty(r3d.attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, torch.bfloat16),
+                     dtype=torch.uint8, device=gpu)
+    want_out, want_lse = r3d.attn_fwd_constmax(q, k, v, scale=scale, workspace=ws)
+    ref_out, ref_lse = r3d.attn_fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    # the recompute made the flagged tiles equal to the online kernel's result
+    assert torch.isfinite(want_out.float()).all() and torch.isfinite(want_lse).all()
+    assert (want_out.float() - ref_out.float()).abs().max().item() <= 2e-2
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=gpu)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r3d.attn_fwd_constmax(q, k, v, scale=scale, out=out, lse=lse, workspace=ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r3d.attn_fwd_constmax(q, k, v, scale=scale, out=out, lse=lse, workspace=ws)
+    other_out = torch.empty_like(q)
+    _replay_and_check(g, [out, lse], [want_out, want_lse],
+                      lambda: r3d.attn_fwd_constmax(q, k_plain, v, scale=scale, out=other_out, workspace=ws))
