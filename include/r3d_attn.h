@@ -174,7 +174,7 @@ R3D_API int r3d_joint_concat_permute_qknorm(const void* const* segs, const int64
  *   those tiles' rows -- the ring's per-shard partial + merge, on one device.
  *   A cost model of the rounds picks the tile height and the split (either
  *   must gain 2%).  The result equals that of any other choice up to
- *   rounding.  r3d_attn_fwd_bshd always uses 384-row tiles and never splits.
+ *   rounding.  r3d_attn_fwd_bshd plans the same way (its merge writes token-major rows).
  * Errors: R3D_EINVAL (NULL/misaligned, sizes <= 0, kv_chunk < 0, non-finite scale,
  * out/lse overlapping an input, a workspace that is NULL, too small, misaligned or
  * overlapping a tensor), R3D_EUNSUPPORTED (D, dtype, or for R3D_BF16 an Sq or Skv
@@ -188,7 +188,7 @@ R3D_API int r3d_attn_fwd(const void* q, const void* k, const void* v, void* out,
 /*
  * r3d_attn_fwd_workspace_size — bytes of workspace r3d_attn_fwd needs for these
  * arguments on the CURRENT device (the key-split decision depends on its number of
- * compute units); r3d_attn_fwd_bshd needs at most as much.  Writes *bytes; performs
+ * compute units); r3d_attn_fwd_bshd needs the same.  Writes *bytes; performs
  * no device work and allocates nothing.
  * Errors: R3D_EINVAL (sizes <= 0, kv_chunk < 0, NULL bytes, overflow),
  * R3D_EUNSUPPORTED (dtype).

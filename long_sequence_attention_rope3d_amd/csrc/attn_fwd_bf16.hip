@@ -930,10 +930,18 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   e = launch_attn_kernel<false>(q, k, v, out, lse, B, H, Sq, Skv, D, scale, kv_chunk, out_bshd, stats, ks, o_parts,
                                 l_parts, nullptr, nullptr, stream);
   if (e != hipSuccess || ks.n_split <= 1) return e;
-  // Merge the pieces' partials into the rows of the split tiles.
+  // Merge the pieces' partials into the rows of the split tiles (token-major
+  // rows for a [B, Sq, H, D] output).
   const int64_t row0 = attn_bf16_split_first_row(ks.n_bulk, Sq, ks.waves);
-  return launch_lse_merge(o_parts, l_parts, ks.n_split, false, static_cast<uint16_t*>(out) + row0 * D,
-                          lse ? lse + row0 : nullptr, true, B * H * Sq - row0, D, stream);
+  TokenMajor tm;
+  if (out_bshd) {
+    tm.row0 = row0;
+    tm.H = H;
+    tm.Sq = Sq;
+  }
+  return launch_lse_merge(o_parts, l_parts, ks.n_split, false,
+                          static_cast<uint16_t*>(out) + (out_bshd ? 0 : row0 * D), lse ? lse + row0 : nullptr, true,
+                          B * H * Sq - row0, D, stream, tm);
 }
 
 hipError_t launch_attn_bf16_constmax(const void* q, const void* k, const void* v, void* out, float* lse,

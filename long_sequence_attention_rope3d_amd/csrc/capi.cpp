@@ -340,14 +340,13 @@ struct AttnPlan {
   }
 };
 
-AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype,
-                   bool out_bshd) {
+AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype) {
   AttnPlan p;
   p.unsplit(B, H, Sq, Skv);
   if (dtype != R3D_BF16) return p;  // the fp32 kernel needs no workspace
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
-  if (!out_bshd) p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
+  p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
   {  // the planned grid must still fit a 1-D launch
     const int64_t tiles = B * H * r3d::attn_bf16_query_tiles(Sq, p.ks.waves);
     const int64_t blocks = p.ks.n_split > 1 ? p.ks.n_bulk + (tiles - p.ks.n_bulk) * p.ks.n_split : tiles;
@@ -378,7 +377,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   int st = check_attn_args(what, q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
   if (st != R3D_OK) return st;
   if (kv_chunk < 0) return fail(R3D_EINVAL, "%s: kv_chunk=%lld < 0", what, (long long)kv_chunk);
-  AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, out_bshd);
+  AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype);
   if (scratch_limit >= 0 && plan.total() > 0) {
     if (plan.stats_bytes > scratch_limit)
       return fail(R3D_EINVAL, "%s: B*H=%lld needs %lld bytes of scratch, more than the %lld available", what,
@@ -429,7 +428,7 @@ R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_
   int64_t bhq;
   if (!product(bhq, {B, H, Sq, D + 1}) || bhq > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd_workspace_size: sizes too large");
-  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, false).total(), bytes);
+  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype).total(), bytes);
 }
 
 R3D_API int r3d_attn_fwd_constmax_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,

@@ -92,7 +92,7 @@ KeySplit attn_bf16_key_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int6
 int64_t attn_bf16_split_first_row(int64_t n_bulk, int64_t Sq, int waves);
 
 // attn_fwd, bf16 MFMA path (D = 64 or 128).  out_bshd: out is [B, Sq, H, D]
-// instead of [B, H, Sq, D] (no key split then).  stats is a device workspace
+// instead of [B, H, Sq, D] (a key split's merge writes it token-major too).  stats is a device workspace
 // of attn_stats_floats(B, H) floats, written by a pre-pass and read by the
 // attention kernel on `stream`.  With ks.n_split > 1, o_parts / l_parts hold
 // the pieces' partials [n_split, rows, D] / [n_split, rows] (rows = B*H*Sq -
@@ -133,8 +133,14 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            int64_t kv_chunk, bool out_bshd, hipStream_t stream);
 
 // lse_merge: parts [n, rows, D] + lse [n, rows] -> out [rows, D] (+ lse_out).
+// With a token-major map (tm.H > 0) merged row r is row g = tm.row0 + r of
+// [B*H*Sq] order, (b, h, s), and goes to row (b*Sq + s)*H + h of out
+// ([B, Sq, H, D]); lse_out stays indexed by r.
+struct TokenMajor {
+  int64_t row0 = 0, H = 0, Sq = 0;
+};
 hipError_t launch_lse_merge(const void* parts, const float* lse_parts, int32_t n, bool parts_bf16,
                             void* out, float* lse_out, bool out_bf16, int64_t rows, int64_t D,
-                            hipStream_t stream);
+                            hipStream_t stream, const TokenMajor& tm = TokenMajor{});
 
 }  // namespace r3d

@@ -47,7 +47,7 @@ template <bool PBF16, bool OBF16>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__ parts,
                                                         const float* __restrict__ lse_parts, int n,
                                                         void* __restrict__ out, float* __restrict__ lse_out,
-                                                        int64_t rows, int D) {
+                                                        int64_t rows, int D, TokenMajor tm) {
   const int cpr = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / cpr;
@@ -104,7 +104,12 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__
       for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, x[e], acc[e]);
     }
   }
-  const int64_t o = row * D + c * 8;
+  int64_t orow = row;
+  if (tm.H > 0) {  // token-major output: row g = (b*H + h)*Sq + s -> (b*Sq + s)*H + h
+    const int64_t g = tm.row0 + row, bh = g / tm.Sq, s = g - bh * tm.Sq, b = bh / tm.H;
+    orow = (b * tm.Sq + s) * tm.H + (bh - b * tm.H);
+  }
+  const int64_t o = orow * D + c * 8;
   if constexpr (OBF16) {
     u32x4 v;
 #pragma unroll
@@ -124,17 +129,18 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const void* __restrict__
 }  // namespace
 
 hipError_t launch_lse_merge(const void* parts, const float* lse_parts, int32_t n, bool parts_bf16, void* out,
-                            float* lse_out, bool out_bf16, int64_t rows, int64_t D, hipStream_t stream) {
+                            float* lse_out, bool out_bf16, int64_t rows, int64_t D, hipStream_t stream,
+                            const TokenMajor& tm) {
   const int64_t threads = rows * (D / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (parts_bf16 && out_bf16)
-    lse_merge_kernel<true, true><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D);
+    lse_merge_kernel<true, true><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D, tm);
   else if (parts_bf16)
-    lse_merge_kernel<true, false><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D);
+    lse_merge_kernel<true, false><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D, tm);
   else if (out_bf16)
-    lse_merge_kernel<false, true><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D);
+    lse_merge_kernel<false, true><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D, tm);
   else
-    lse_merge_kernel<false, false><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D);
+    lse_merge_kernel<false, false><<<blocks, 256, 0, stream>>>(parts, lse_parts, n, out, lse_out, rows, (int)D, tm);
   return hipGetLastError();
 }
 

@@ -637,6 +637,30 @@ def test_attn_bshd_is_the_bhsd_result_relaid(gpu, dtype, D, B, H, Sq, Skv, kv_ch
     assert torch.equal(la, lb)
 
 
+@pytest.mark.parametrize("B,H,Sq,Skv,kv_chunk", [
+    (1, 24, 4352, 4352, 0),     # 256 whole 12-wave tiles, the last 32 split over key ranges
+    (2, 12, 4352, 4352, 0),     # the same grid over two batches: split rows of batch 1
+    (1, 4, 300, 9000, 0),       # few tiles: 8-wave blocks, every tile split
+])
+def test_attn_bshd_key_split(gpu, B, H, Sq, Skv, kv_chunk):
+    """A key-split launch with token-major output: the merge writes the split tiles'
+    rows to [B, Sq, H, D]; the result is the [B, H, Sq, D] call's, relaid, bit for bit."""
+    D = 128
+    say(f"bshd split B={B} H={H} Sq={Sq} Skv={Skv} chunk={kv_chunk}")
+    # a split is planned: the workspace holds partials beyond the 512 bytes per head
+    assert r3d.attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, torch.bfloat16) > 512 * B * H
+    q = _rand((B, H, Sq, D), torch.bfloat16, 84).to(gpu)
+    k = _rand((B, H, Skv, D), torch.bfloat16, 85).to(gpu)
+    v = _rand((B, H, Skv, D), torch.bfloat16, 86).to(gpu)
+    a, la = r3d.attn_fwd(q, k, v, kv_chunk=kv_chunk)
+    b = torch.full((B, Sq, H, D), float("nan"), dtype=torch.bfloat16, device=gpu)
+    lb = torch.full((B, H, Sq), float("nan"), device=gpu)
+    r3d.attn_fwd(q, k, v, kv_chunk=kv_chunk, out=b, lse=lb, out_layout="bshd")
+    torch.cuda.synchronize()
+    assert torch.equal(b, a.transpose(1, 2).contiguous())
+    assert torch.equal(la, lb)
+
+
 def test_attn_bshd_matches_oracle(gpu):
     q = _rand((2, 3, 200, 128), torch.bfloat16, 91)
     k = _rand((2, 3, 450, 128), torch.bfloat16, 92)
