@@ -68,3 +68,50 @@ def test_lse_merge_runs_on_the_current_stream(gpu):
     assert not side.query()
     side.synchronize()
     assert torch.equal(out, want) and torch.equal(lse, want_lse)
+
+
+def test_attn_fwd_from_two_host_threads(gpu):
+    """Two host threads each issue attn_fwd calls on their own stream with their own
+    workspace and buffers (the library keeps no per-call state between calls; its error
+    text is per thread): every result equals the single-threaded call, bit for bit, and
+    a call that fails in one thread leaves the other thread's error text alone."""
+    import threading
+    shapes = [(1, 24, 4352, 128, 0), (1, 4, 300, 128, 1024)]   # a split 12-wave grid; an 8-wave split grid
+    cases = []
+    for i, (B, H, S, D, ch) in enumerate(shapes):
+        q, k, v = (_rand((B, H, S if j == 0 else S + 700 * i, D), 30 + 3 * i + j).to(gpu) for j in range(3))
+        want = r3d.attn_fwd(q, k, v, kv_chunk=ch)
+        cases.append((q, k, v, ch, want))
+    torch.cuda.synchronize()
+    errors, msgs = [], {}
+
+    def worker(idx):
+        try:
+            q, k, v, ch, (want_o, want_l) = cases[idx]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                ws = torch.empty(r3d.attn_fwd_workspace_size(*q.shape[:3], k.shape[2], q.shape[3], ch,
+                                                             torch.bfloat16), dtype=torch.uint8, device=gpu)
+                for _ in range(5):
+                    o, l = r3d.attn_fwd(q, k, v, kv_chunk=ch, workspace=ws)
+                    s.synchronize()
+                    if not (torch.equal(o, want_o) and torch.equal(l, want_l)):
+                        errors.append(f"thread {idx}: result differs")
+                if idx == 0:
+                    try:
+                        r3d.attn_fwd(q, k, v, kv_chunk=-1)
+                    except ValueError as e:
+                        msgs[idx] = str(e)
+                else:
+                    msgs[idx] = r3d._lib.r3d_last_error().decode()
+        except Exception as e:  # noqa: BLE001 (reported below)
+            errors.append(f"thread {idx}: {e!r}")
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in ts), "a worker thread did not finish"
+    assert not errors, errors
+    assert "kv_chunk" in msgs[0] and msgs[1] == ""
