@@ -466,7 +466,7 @@ def test_attn_key_split_small(gpu, D, B, H, Sq, Skv, kv_chunk):
     chunks, or whole tiles with a single chunk), write fp32 partials and merge them with
     lse_merge.  These shapes split (the grid is far below one round of the CUs); the
     result must match the oracle like any other call, and the token-major entry point,
-    which does not split, must agree with it."""
+    which splits the same way, must give the same values bit for bit."""
     scale = 1.0 / math.sqrt(D)
     q = _rand((B, H, Sq, D), torch.bfloat16, 61)
     k = _rand((B, H, Skv, D), torch.bfloat16, 62)
@@ -476,7 +476,7 @@ def test_attn_key_split_small(gpu, D, B, H, Sq, Skv, kv_chunk):
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale)
     check_attn(out, lse, ref_out, ref_lse, torch.bfloat16, f"split D={D} Skv={Skv} kv_chunk={kv_chunk}")
-    check_attn(ob.transpose(1, 2), lb, ref_out, ref_lse, torch.bfloat16, "unsplit bshd")
+    assert torch.equal(ob, out.transpose(1, 2).contiguous()) and torch.equal(lb, lse)
     # Without an lse output the merge still weighs the parts by their (workspace) lse.
     o2 = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=kv_chunk, return_lse=False)
     assert torch.equal(o2, out)
