@@ -28,15 +28,36 @@ constexpr int kRowsF32 = 4;          // query rows (waves) per block
 constexpr int kBNF32 = 64;           // keys per tile: one per lane
 constexpr int kThreadsF32 = 64 * kRowsF32;
 
+// Wave-wide max and sum (the result wave-uniform).  DPP row rotations
+// (row_ror 8, 4, 2, 1 within each row of 16 lanes: register reads, no LDS
+// round trip) leave every lane of a row with its row's result; lanes 0, 16,
+// 32 and 48 are then read into scalars and combined.
+template <int kRor>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + kRor, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float rows_of(float x, float (*op)(float, float)) {
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float max2(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float add2(float a, float b) { return a + b; }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  x = fmaxf(x, row_ror<1>(x));
+  return rows_of(x, max2);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  return rows_of(x, add2);
 }
 
 template <int D>
