@@ -29,34 +29,37 @@ def _replay_and_check(graph, outputs, want, perturb):
             assert torch.equal(o, w), f"replay {r}"
 
 
-@pytest.mark.parametrize("shape", [
-    (1, 24, 4352, 4352, 128, 0),     # 256 whole 12-wave tiles + 32 split 7 ways: pre-pass, attention, merge
-    (1, 4, 300, 9000, 128, 0),       # few tiles: 8-wave blocks, every tile split
-    (1, 2, 700, 1300, 64, 1024),     # D = 64, two chunks
+@pytest.mark.parametrize("shape,layout", [
+    ((1, 24, 4352, 4352, 128, 0), "bhsd"),   # 256 whole 12-wave tiles + 32 split 7 ways: pre-pass, attention, merge
+    ((1, 24, 4352, 4352, 128, 0), "bshd"),   # the same with token-major output (the merge writes token-major rows)
+    ((1, 4, 300, 9000, 128, 0), "bhsd"),     # few tiles: 8-wave blocks, every tile split
+    ((1, 2, 700, 1300, 64, 1024), "bhsd"),   # D = 64, two chunks
 ])
-def test_attn_fwd_graph_replay(gpu, shape):
+def test_attn_fwd_graph_replay(gpu, shape, layout):
     B, H, Sq, Skv, D, kv_chunk = shape
     q, k, v = (_rand((B, H, S, D), torch.bfloat16, 40 + i).to(gpu) for i, S in enumerate((Sq, Skv, Skv)))
     scale = 1.0 / math.sqrt(D)
     ws = torch.empty(max(1, r3d.attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, torch.bfloat16)),
                      dtype=torch.uint8, device=gpu)
-    out = torch.empty_like(q)
+    oshape = (B, H, Sq, D) if layout == "bhsd" else (B, Sq, H, D)
+    out = torch.empty(oshape, dtype=torch.bfloat16, device=gpu)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=gpu)
-    want_out, want_lse = r3d.attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, workspace=ws)
+    call = lambda o, l: r3d.attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, out=o, lse=l,  # noqa: E731
+                                     workspace=ws, out_layout=layout)
+    want_out, want_lse = call(None, None)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        r3d.attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, out=out, lse=lse, workspace=ws)  # warm-up
+        call(out, lse)  # warm-up
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        r3d.attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, out=out, lse=lse, workspace=ws)
+        call(out, lse)
     # between replays, an eager call of its own overwrites the workspace
-    other_out = torch.empty_like(q)
-    _replay_and_check(g, [out, lse], [want_out, want_lse],
-                      lambda: r3d.attn_fwd(q, k, v, scale=scale, kv_chunk=kv_chunk, out=other_out, workspace=ws))
+    other_out = torch.empty(oshape, dtype=torch.bfloat16, device=gpu)
+    _replay_and_check(g, [out, lse], [want_out, want_lse], lambda: call(other_out, None))
 
 
 def test_permute_and_merge_graph_replay(gpu):
