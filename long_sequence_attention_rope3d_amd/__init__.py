@@ -135,7 +135,15 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+# torch's current stream of a device as a raw handle, without building a
+# torch.cuda.Stream object per call (~0.2 instead of ~2 us on the host);
+# the public route where that query is not available.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
