@@ -197,6 +197,33 @@ R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_
                                         int64_t kv_chunk, int32_t dtype, size_t* bytes);
 
 /*
+ * r3d_attn_fwd_plan — the launch plan r3d_attn_fwd (and r3d_attn_fwd_bshd) would use for
+ * R3D_BF16 arguments on a device with n_cus compute units (0: unknown, which plans no key
+ * split): the tile height and the key split described under r3d_attn_fwd (the ring's
+ * per-shard partials and their log-sum-exp merge, "Context Parallelism in vLLM Omni
+ * Neuron", §Ring attention).  A host query: performs no device work, allocates nothing.
+ *   plan->waves           waves per block; a query tile is 32 * waves rows of one head
+ *   plan->n_tiles         query tiles, B * H * ceil(Sq / (32 * waves)), head-major
+ *   plan->n_bulk          tiles [0, n_bulk) run over all keys in one block each
+ *   plan->n_split         tiles [n_bulk, n_tiles) run as n_split blocks over key ranges
+ *                         of split_len keys (1: no split, n_bulk = n_tiles)
+ *   plan->split_len       keys per range (a whole number of kv_chunk chunks)
+ *   plan->workspace_bytes r3d_attn_fwd's workspace for this plan
+ * Errors: R3D_EINVAL (NULL plan, sizes <= 0, kv_chunk or n_cus < 0, sizes too large),
+ * R3D_EUNSUPPORTED (D, or Sq or Skv above 2^31 - 1024).
+ */
+typedef struct r3d_attn_plan {
+  int32_t waves;
+  int32_t n_split;
+  int64_t n_tiles;
+  int64_t n_bulk;
+  int64_t split_len;
+  int64_t workspace_bytes;
+} r3d_attn_plan;
+R3D_API int r3d_attn_fwd_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                              int32_t n_cus, r3d_attn_plan* plan);
+
+/*
  * r3d_attn_fwd_noalloc — r3d_attn_fwd without a workspace argument and without any
  * allocation, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc).  Its scratch is a

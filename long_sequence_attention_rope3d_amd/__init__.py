@@ -15,6 +15,7 @@ Calls (same names as the C entry points without the ``r3d_`` prefix):
   attn_fwd(q, k, v, scale=None, kv_chunk=0, out=None, lse=None, return_lse=True,
            out_layout="bhsd", workspace=None)
   attn_fwd_workspace_size(B, H, Sq, Skv, D, kv_chunk, dtype)
+  attn_fwd_plan(B, H, Sq, Skv, D, kv_chunk, n_cus)
   attn_fwd_constmax(q, k, v, scale=None, out=None, lse=None, workspace=None)
   attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, dtype)
   lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None)
@@ -34,7 +35,8 @@ from typing import Optional, Sequence, Tuple
 
 import torch
 
-__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_noalloc",
+__all__ = ["rope3d_apply", "joint_concat_permute", "attn_fwd", "attn_fwd_workspace_size", "attn_fwd_plan",
+           "attn_fwd_noalloc",
            "attn_fwd_constmax",
            "attn_fwd_constmax_workspace_size", "lse_merge", "joint_attention", "Rope3D", "library_path", "R3D_OK",
            "R3D_EINVAL", "R3D_EUNSUPPORTED", "R3D_EHIP"]
@@ -58,6 +60,11 @@ class _RopeDesc(ctypes.Structure):
                 ("theta", ctypes.c_double)]
 
 
+class _AttnPlan(ctypes.Structure):
+    _fields_ = [("waves", ctypes.c_int32), ("n_split", ctypes.c_int32), ("n_tiles", ctypes.c_int64),
+                ("n_bulk", ctypes.c_int64), ("split_len", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -77,10 +84,11 @@ def _load():
     lib.r3d_attn_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
     lib.r3d_attn_fwd_constmax.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_float, I32, P, SZ, P]
     lib.r3d_attn_fwd_constmax_workspace_size.argtypes = [I64, I64, I64, I64, I64, I32, ctypes.POINTER(SZ)]
+    lib.r3d_attn_fwd_plan.argtypes = [I64, I64, I64, I64, I64, I64, I32, ctypes.POINTER(_AttnPlan)]
     lib.r3d_lse_merge.argtypes = [P, P, I32, I32, P, P, I32, I64, I64, I64, I64, P]
     for f in ("r3d_rope3d_apply", "r3d_joint_concat_permute", "r3d_joint_concat_permute_qknorm",
               "r3d_attn_fwd", "r3d_attn_fwd_bshd", "r3d_attn_fwd_noalloc", "r3d_attn_fwd_workspace_size",
-              "r3d_attn_fwd_constmax",
+              "r3d_attn_fwd_constmax", "r3d_attn_fwd_plan",
               "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge"):
         getattr(lib, f).restype = ctypes.c_int
     lib.r3d_last_error.restype = ctypes.c_char_p
@@ -264,6 +272,15 @@ def attn_fwd_constmax_workspace_size(B: int, H: int, Sq: int, Skv: int, D: int, 
     _check(_lib.r3d_attn_fwd_constmax_workspace_size(B, H, Sq, Skv, D, _DTYPES[dtype], ctypes.byref(n)),
            "attn_fwd_constmax_workspace_size")
     return int(n.value)
+
+
+def attn_fwd_plan(B: int, H: int, Sq: int, Skv: int, D: int, kv_chunk: int, n_cus: int) -> dict:
+    """The bf16 launch plan attn_fwd would use on a device with n_cus compute units
+    (r3d_attn_fwd_plan): waves per block, query tiles, whole tiles, key ranges per split
+    tile, keys per range and the workspace bytes."""
+    p = _AttnPlan()
+    _check(_lib.r3d_attn_fwd_plan(B, H, Sq, Skv, D, kv_chunk, n_cus, ctypes.byref(p)), "attn_fwd_plan")
+    return {f: getattr(p, f) for f, _ in _AttnPlan._fields_}
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,

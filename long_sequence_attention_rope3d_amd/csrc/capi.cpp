@@ -340,13 +340,15 @@ struct AttnPlan {
   }
 };
 
-AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype) {
+// n_cus: compute units of the device the call runs on (0: unknown, no key split).
+AttnPlan plan_attn(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk, int32_t dtype,
+                   int n_cus) {
   AttnPlan p;
   p.unsplit(B, H, Sq, Skv);
   if (dtype != R3D_BF16) return p;  // the fp32 kernel needs no workspace
   const int64_t chunk = (kv_chunk == 0 || kv_chunk >= Skv) ? Skv : kv_chunk;
   p.stats_bytes = ws_round(r3d::attn_stats_floats(B, H) * 4);
-  p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, device_cus());
+  p.ks = r3d::attn_bf16_key_split(B, H, Sq, Skv, D, chunk, n_cus);
   {  // the planned grid must still fit a 1-D launch
     const int64_t tiles = B * H * r3d::attn_bf16_query_tiles(Sq, p.ks.waves);
     const int64_t blocks = p.ks.n_split > 1 ? p.ks.n_bulk + (tiles - p.ks.n_bulk) * p.ks.n_split : tiles;
@@ -377,7 +379,7 @@ int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
   int st = check_attn_args(what, q, k, v, out, lse, B, H, Sq, Skv, D, scale, dtype, nq, nk, bhq);
   if (st != R3D_OK) return st;
   if (kv_chunk < 0) return fail(R3D_EINVAL, "%s: kv_chunk=%lld < 0", what, (long long)kv_chunk);
-  AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype);
+  AttnPlan plan = plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, device_cus());
   if (scratch_limit >= 0 && plan.total() > 0) {
     if (plan.stats_bytes > scratch_limit)
       return fail(R3D_EINVAL, "%s: B*H=%lld needs %lld bytes of scratch, more than the %lld available", what,
@@ -428,7 +430,29 @@ R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_
   int64_t bhq;
   if (!product(bhq, {B, H, Sq, D + 1}) || bhq > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd_workspace_size: sizes too large");
-  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype).total(), bytes);
+  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, device_cus()).total(), bytes);
+}
+
+R3D_API int r3d_attn_fwd_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
+                              int32_t n_cus, r3d_attn_plan* plan) {
+  if (!plan) return fail(R3D_EINVAL, "attn_fwd_plan: NULL result pointer");
+  if (B <= 0 || H <= 0 || Sq <= 0 || Skv <= 0 || D <= 0 || kv_chunk < 0 || n_cus < 0)
+    return fail(R3D_EINVAL, "attn_fwd_plan: B, H, Sq, Skv, D must be > 0, kv_chunk and n_cus >= 0");
+  if (D != 64 && D != 128) return fail(R3D_EUNSUPPORTED, "attn_fwd_plan: D=%lld (supported: 64, 128)", (long long)D);
+  if (Sq > r3d::kAttnMaxSeq || Skv > r3d::kAttnMaxSeq)
+    return fail(R3D_EUNSUPPORTED, "attn_fwd_plan: Sq=%lld, Skv=%lld (at most %lld each)", (long long)Sq,
+                (long long)Skv, (long long)r3d::kAttnMaxSeq);
+  int64_t bhq;
+  if (!product(bhq, {B, H, Sq, D + 1}) || bhq > kMaxElems || !r3d::attn_bf16_launches_fit(B, H, Sq))
+    return fail(R3D_EINVAL, "attn_fwd_plan: sizes too large");
+  const AttnPlan p = plan_attn(B, H, Sq, Skv, D, kv_chunk, R3D_BF16, n_cus);
+  plan->waves = p.ks.waves;
+  plan->n_split = p.ks.n_split;
+  plan->n_tiles = B * H * r3d::attn_bf16_query_tiles(Sq, p.ks.waves);
+  plan->n_bulk = p.ks.n_bulk;
+  plan->split_len = p.ks.split_len;
+  plan->workspace_bytes = p.total();
+  return ok();
 }
 
 R3D_API int r3d_attn_fwd_constmax_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,

@@ -31,8 +31,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted(["r3d_rope3d_apply", "r3d_joint_concat_permute",
                                   "r3d_joint_concat_permute_qknorm", "r3d_attn_fwd", "r3d_attn_fwd_bshd",
                                   "r3d_attn_fwd_noalloc", "r3d_attn_fwd_workspace_size", "r3d_attn_fwd_constmax",
-                                  "r3d_attn_fwd_constmax_workspace_size", "r3d_lse_merge", "r3d_last_error",
-                                  "r3d_version"])
+                                  "r3d_attn_fwd_constmax_workspace_size", "r3d_attn_fwd_plan", "r3d_lse_merge",
+                                  "r3d_last_error", "r3d_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -268,3 +268,67 @@ def test_binding_rejects_host_tensors():
         r3d.attn_fwd(q, q, q)
     with pytest.raises(ValueError, match="out_layout"):
         r3d.attn_fwd(q, q, q, out_layout="sbhd")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("waves", ctypes.c_int32), ("n_split", ctypes.c_int32), ("n_tiles", ctypes.c_int64),
+                ("n_bulk", ctypes.c_int64), ("split_len", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+LIB.r3d_attn_fwd_plan.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int32, ctypes.POINTER(_Plan)]
+LIB.r3d_attn_fwd_plan.restype = ctypes.c_int
+
+
+def _plan(B, H, Sq, Skv, D, kv_chunk, n_cus):
+    p = _Plan()
+    st = LIB.r3d_attn_fwd_plan(B, H, Sq, Skv, D, kv_chunk, n_cus, ctypes.byref(p))
+    return st, p
+
+
+@pytest.mark.parametrize("name,args,want", [
+    # (B, H, Sq, Skv, D, kv_chunk) -> (waves, n_tiles, n_bulk, n_split, split_len) on 256 CUs
+    ("pro-clip", (1, 24, 52608, 52608, 128, 4096), (12, 3288, 3288, 1, 52608)),     # last round 84% full
+    ("image-dit", (1, 24, 4352, 4352, 128, 0), (12, 288, 256, 7, 640)),
+    ("long-video", (1, 24, 119056, 119056, 128, 8192), (12, 7464, 7424, 5, 24576)),  # 3 chunks a range
+    ("lite-clip", (1, 16, 3216, 3216, 128, 512), (8, 208, 208, 1, 3216)),           # 8-wave tiles, one round
+    ("Ulysses rank", (1, 3, 52608, 52608, 128, 4096), (12, 411, 256, 13, 4096)),    # one chunk a range
+    ("CP rank", (1, 24, 6576, 52608, 128, 6576), (12, 432, 256, 4, 13152)),         # two chunks a range
+])
+def test_attn_fwd_plan_on_256_cus(name, args, want):
+    """The key-split planner's choice for each workload and shard shape on the MI355X's
+    256 CUs (host logic; the GPU tests run these plans): a thin last round of query
+    tiles is split into key ranges of whole chunks, a grid of few tiles takes 8-wave
+    blocks, and the workspace holds the statistics plus the split tiles' partials."""
+    st, p = _plan(*args, 256)
+    assert st == 0, LIB.r3d_last_error()
+    assert (p.waves, p.n_tiles, p.n_bulk, p.n_split, p.split_len) == want, name
+    B, H, Sq, Skv, D, _ = args
+    stats = -(-2 * B * H * 64 * 4 // 256) * 256
+    if p.n_split == 1:
+        assert p.workspace_bytes == stats
+    else:
+        rows_per_tile = 32 * p.waves
+        first_row = (p.n_bulk // (p.n_tiles // (B * H))) * Sq + (p.n_bulk % (p.n_tiles // (B * H))) * rows_per_tile
+        rows = B * H * Sq - first_row
+        assert p.workspace_bytes == stats + -(-p.n_split * rows * (D + 1) * 4 // 256) * 256
+
+
+def test_attn_fwd_plan_without_a_device_count_and_rejects():
+    """n_cus = 0 (unknown device) plans no split, which is what the workspace query gives
+    on a host without a GPU; bad arguments are refused."""
+    st, p = _plan(1, 24, 4352, 4352, 128, 0, 0)
+    assert st == 0 and p.waves == 12 and p.n_split == 1 and p.n_bulk == p.n_tiles == 288
+    n = ctypes.c_size_t(0)
+    assert LIB.r3d_attn_fwd_workspace_size(1, 24, 4352, 4352, 128, 0, 1, ctypes.byref(n)) == 0
+    assert n.value == p.workspace_bytes
+    assert _plan(1, 24, 4352, 4352, 128, 0, -1)[0] == -1
+    assert _plan(1, 24, 4352, 4352, 96, 0, 256)[0] == -2
+    assert LIB.r3d_attn_fwd_plan(1, 2, 64, 64, 128, 0, 256, None) == -1
+    assert "NULL" in LIB.r3d_last_error().decode()
+
+
+def test_binding_attn_fwd_plan():
+    p = r3d.attn_fwd_plan(1, 24, 4352, 4352, 128, 0, 256)
+    assert (p["waves"], p["n_tiles"], p["n_bulk"], p["n_split"], p["split_len"]) == (12, 288, 256, 7, 640)
+    with pytest.raises(ValueError, match="n_cus"):
+        r3d.attn_fwd_plan(1, 24, 4352, 4352, 128, 0, -1)
