@@ -98,7 +98,12 @@ __global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __re
     }
   };
 
-  float L = -INFINITY;
+  // The running result's log-sum-exp L and each chunk's lse_c are kept in
+  // fp64 (by additions only): their difference sets the merge weights, and
+  // in fp32 a value near ln Skv would carry ~1e-6 absolute error into every
+  // merge.  The transcendental steps stay in fp32 on small arguments: ln of
+  // l's mantissa (in [0.5, 1)), and e^-|L - lse_c| with its log1p.
+  double L = -INFINITY;
   float o[E], acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = acc[e] = 0.f;
@@ -163,11 +168,26 @@ __global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __re
 
     if (chunk_end) {
       // explicit log-sum-exp merge of this chunk into the running result
-      const float lse_c = m + logf(l);
-      const float hi = fmaxf(L, lse_c);
-      const float Ln = (L == -INFINITY) ? lse_c : hi + logf(expf(L - hi) + expf(lse_c - hi));
-      const float wa = expf(L - Ln);
-      const float wb = expf(lse_c - Ln) / l;
+      int le;
+      const float lm = frexpf(l, &le);  // l = lm 2^le (l >= 1: the row max's p is 1)
+      const double lse_c = (double)m + (double)le * 0.69314718055994530942 + (double)logf(lm);
+      // L' = max + ln(1 + t), t = e^-|L - lse_c|; the weights of the two
+      // results are 1 / (1 + t) and t / (1 + t) (wb also divides by l).
+      double Ln;
+      float wa, wb;
+      if (L == -INFINITY) {
+        Ln = lse_c;
+        wa = 0.f;
+        wb = 1.0f / l;
+      } else {
+        const double d = L - lse_c;
+        const float t = expf(-(float)fabs(d));
+        const float r = 1.0f / (1.0f + t);
+        Ln = fmax(L, lse_c) + (double)log1pf(t);
+        const bool keep = d >= 0.0;  // the running result is the larger
+        wa = keep ? r : t * r;
+        wb = (keep ? t * r : r) / l;
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         o[e] = o[e] * wa + acc[e] * wb;
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(kThreadsF32) void attn_f32_kernel(const float* __re
     const int64_t orow = out_bshd ? (b * Sq + qi) * H + (bh - b * H) : bh * Sq + qi;
 #pragma unroll
     for (int e = 0; e < E; ++e) out[orow * D + lane + 64 * e] = o[e];
-    if (lse && lane == 0) lse[bh * Sq + qi] = L;
+    if (lse && lane == 0) lse[bh * Sq + qi] = (float)L;
   }
 }
 

@@ -677,6 +677,25 @@ def test_attn_bshd_matches_oracle(gpu):
 # GPU invariants
 # ------------------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attn_fwd_a_thousand_chunks(gpu, dtype):
+    """1024 KV chunks per row (Skv = 65536, kv_chunk = 64): the running result is
+    normalised and carried through a thousand log-sum-exp merges (the workloads have at
+    most 15).  Sampled rows against the oracle's unchunked attention."""
+    B, H, Sq, Skv, D = 1, 2, 400, 65536, 128 if dtype == torch.bfloat16 else 64
+    scale = 1.0 / math.sqrt(D)
+    q = _rand((B, H, Sq, D), dtype, 141)
+    k = _rand((B, H, Skv, D), dtype, 142)
+    v = _rand((B, H, Skv, D), dtype, 143)
+    out, lse = r3d.attn_fwd(q.to(gpu), k.to(gpu), v.to(gpu), scale=scale, kv_chunk=64)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(144).choice(B * H * Sq, 48, replace=False))
+    ref_out, ref_lse = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), rows, scale)
+    got_out = out.reshape(B * H * Sq, D)[torch.from_numpy(rows).to(gpu)]
+    got_lse = lse.reshape(B * H * Sq)[torch.from_numpy(rows).to(gpu)]
+    check_attn(got_out, got_lse, ref_out, ref_lse, dtype, f"1024 chunks {dtype}")
+
+
 def test_attn_fwd_deterministic_and_chunk_invariant(gpu):
     q = _rand((1, 4, 700, 128), torch.bfloat16, 61).to(gpu)
     k = _rand((1, 4, 3000, 128), torch.bfloat16, 62, 2.0).to(gpu)
