@@ -35,6 +35,7 @@ import math
 import os
 import re
 import statistics
+import subprocess
 import sys
 import time
 
@@ -109,6 +110,17 @@ def _mfma_counters_for_current_kernel():
     return vals
 
 
+def power_cap_watts():
+    """The board's power cap (W) from a read-only SMI query, or None: the attention kernel
+    runs at the clock this cap allows, so boxes with different caps differ in ms per call."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", out)
+    return float(m.group(1)) if m else None
+
+
 def cpu_baseline(w, inp, n_rows: int):
     """The fp64 oracle, as it is, on a bounded sample: RoPE of all of Q and K,
     the re-layout, then attention for n_rows query rows spread over every
@@ -147,6 +159,10 @@ def main():
         print(f"bench.py: this library runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note, not part of this library).", file=sys.stderr)
         sys.exit(2)
+
+    # The board's power cap, read before this process touches the GPU (the query runs
+    # as a child process).
+    power_cap = power_cap_watts()
 
     import torch
     import long_sequence_attention_rope3d_amd as r3d
@@ -243,7 +259,8 @@ def main():
         "attn_ms_per_call": round(attn_avg_ms, 4),
         "attn_ms_median": round(statistics.median(attn_ms), 4),
         "attn_ms_min": round(min(attn_ms), 4),
-        "device": {"name": props.name, "compute_units": props.multi_processor_count},
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "power_cap_w": power_cap},
         "attn_tflops": round(achieved, 2),
         "pct_bf16_peak": round(100 * achieved / MI355X_BF16_PEAK_TFLOPS, 2),
         "roofline": roofline,

@@ -86,3 +86,20 @@ def test_power_figures_follow_the_kernel_hash(tmp_path, monkeypatch):
     power.write_text("kernel_code_sha256: " + "0" * 64 + "\npackage_power_w_under_load: 1349\npower_cap_w: 1400\n")
     c = b._mfma_counters_for_current_kernel()
     assert "package_power_w_under_load" not in c and c["mfma_busy_frac"] == 0.67
+
+
+def test_power_cap_query_parses_the_smi_line(monkeypatch):
+    """The bench records the board's power cap from `rocm-smi --showmaxpower`; a host
+    without the tool (or with other output) gives None."""
+    import subprocess as sp
+    import bench
+
+    class _Done:
+        stdout = "GPU[0]\t\t: Max Graphics Package Power (W): 1400.0\n"
+    monkeypatch.setattr(sp, "run", lambda *a, **k: _Done())
+    assert bench.power_cap_watts() == 1400.0
+
+    def _missing(*a, **k):
+        raise FileNotFoundError("rocm-smi")
+    monkeypatch.setattr(sp, "run", _missing)
+    assert bench.power_cap_watts() is None
