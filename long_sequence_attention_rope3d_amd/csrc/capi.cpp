@@ -430,7 +430,8 @@ R3D_API int r3d_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_
   int64_t bhq;
   if (!product(bhq, {B, H, Sq, D + 1}) || bhq > kMaxElems)
     return fail(R3D_EINVAL, "attn_fwd_workspace_size: sizes too large");
-  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, device_cus()).total(), bytes);
+  return ws_size_out("attn_fwd_workspace_size", plan_attn(B, H, Sq, Skv, D, kv_chunk, dtype, device_cus()).total(),
+                     bytes);
 }
 
 R3D_API int r3d_attn_fwd_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, int64_t kv_chunk,
